@@ -1,0 +1,10 @@
+"""CPU oracle (test infrastructure only; see attention_ref)."""
+from .attention_ref import (  # noqa: F401
+    State,
+    attention_ref,
+    block_state,
+    empty_state,
+    finalize_state,
+    merge_states,
+    online_blocked_ref,
+)

@@ -1,0 +1,158 @@
+"""Plain float64 CPU oracle for the attention forward pass.
+
+TEST INFRASTRUCTURE, NOT PRODUCT CODE.  Only the test-suite, the smoke check
+and the benchmark's CPU-baseline leg may import this module.  It shares no
+code with the HIP path and never calls it.
+
+Sources (cited by page title and section):
+
+  [ES] unite.ai, "Atención Flash: Revolucionando la Eficiencia de los Modelos
+       de Transformador".  The opening code block defines standard attention;
+       section "La Matemática detrás de la Atención Flash" gives the safe
+       softmax (formula 1) and the softmax merge (formula 2); section "Detalles
+       de Implementación" gives a simplified blocked loop with running M and L.
+  [IT] nisoo.com, "Un'immersione approfondita nell'algoritmo FlashAttention –
+       parte 3", sections "Softmax Sicura" and "SafeSoftmax con Calcolo
+       Normalizzatore Online".
+
+What is computed (the plain definition, [ES] standard attention; [ES] formula
+1 and [IT] "Softmax Sicura" for the max subtraction), per head, in float64:
+
+    S = scale * Q K^T          (the score matrix, materialised row chunk by chunk)
+    m_i = max_j S_ij
+    P_ij = exp(S_ij - m_i)
+    l_i = sum_j P_ij
+    O_i = (sum_j P_ij V_j) / l_i
+    LSE_i = m_i + ln l_i       (natural log, in units of the scaled scores)
+
+Readings where the pages are garbled or silent:
+  * [ES] formula 2 (the merge) lost its normalisers in extraction.  The merge
+    used here keeps, per query row, the triple (m, l, O~) with O~ the
+    *unnormalised* weighted sum, and combines two triples with the factors
+    exp(m_x - m) and exp(m_y - m), m = max(m_x, m_y); an empty triple is
+    (-inf, 0, 0).
+  * The simplified loop of [ES] "Detalles de Implementación" stores O already
+    divided by the new L and later rescales it by the max correction alone,
+    which drops the old L; the running form below keeps O~ unnormalised and
+    divides once at the end.
+  * The scale is an explicit argument; the workloads use 1/sqrt(d).  The value
+    given is used as is (callers pass the float32 value the kernel receives).
+  * The log-sum-exp is not on the pages; it is LSE above.
+
+Every function here is pinned by tests against closed forms, invariants, an
+independent library attention routine, hand-derived fixtures and brute force
+over block partitions (the merge); nothing is "parity unpinned".
+"""
+from __future__ import annotations
+
+from typing import NamedTuple
+
+import numpy as np
+
+
+def _f64(x) -> np.ndarray:
+    return np.asarray(x, dtype=np.float64)
+
+
+def _head_rows(q, k, v, scale):
+    """Definition above for one block of query rows against a head's K, V."""
+    s = scale * (q @ k.T)                      # S, fp64
+    m = s.max(axis=1, keepdims=True)           # m_i
+    p = np.exp(s - m)                          # P_ij
+    l = p.sum(axis=1, keepdims=True)           # l_i
+    o = (p @ v) / l                            # O_i
+    lse = m[:, 0] + np.log(l[:, 0])            # LSE_i
+    return o, lse
+
+
+def attention_ref(q, k, v, scale, rows=None, chunk=1024):
+    """Exact attention forward in float64.
+
+    q, k, v: arrays (B, H, N, d) of any float dtype (upcast exactly to fp64).
+    rows:    None for every query row, or flat indices into (B, H, N).
+    Returns (O, LSE): O (B, H, N, d) and LSE (B, H, N); with ``rows``,
+    O (R, d) and LSE (R,) in the order of ``rows``.
+    """
+    q, k, v = _f64(q), _f64(k), _f64(v)
+    B, H, N, d = q.shape
+    if rows is None:
+        o = np.empty((B, H, N, v.shape[-1]))
+        lse = np.empty((B, H, N))
+        for b in range(B):
+            for h in range(H):
+                for i0 in range(0, N, chunk):
+                    i1 = min(i0 + chunk, N)
+                    o[b, h, i0:i1], lse[b, h, i0:i1] = _head_rows(q[b, h, i0:i1], k[b, h], v[b, h], scale)
+        return o, lse
+    rows = np.asarray(rows, dtype=np.int64)
+    o = np.empty((rows.size, v.shape[-1]))
+    lse = np.empty(rows.size)
+    heads = rows // N
+    for hid in np.unique(heads):
+        sel = np.nonzero(heads == hid)[0]
+        b, h = divmod(int(hid), H)
+        o[sel], lse[sel] = _head_rows(q[b, h, rows[sel] % N], k[b, h], v[b, h], scale)
+    return o, lse
+
+
+class State(NamedTuple):
+    """Running per-row softmax state: max m, normaliser l, unnormalised output."""
+    m: np.ndarray   # (R,)
+    l: np.ndarray   # (R,)
+    o: np.ndarray   # (R, dv)
+
+
+def empty_state(rows: int, dv: int) -> State:
+    return State(np.full(rows, -np.inf), np.zeros(rows), np.zeros((rows, dv)))
+
+
+def _factor(m_part, m):
+    """exp(m_part - m), defined as 0 for an empty part (m_part = -inf)."""
+    out = np.zeros_like(m)
+    live = np.isfinite(m_part)
+    out[live] = np.exp(m_part[live] - m[live])
+    return out
+
+
+def block_state(q, k, v, scale) -> State:
+    """State of one key block on its own ([IT] "Softmax Sicura" applied per block)."""
+    q, k, v = _f64(q), _f64(k), _f64(v)
+    s = scale * (q @ k.T)
+    m = s.max(axis=1)
+    p = np.exp(s - m[:, None])
+    return State(m, p.sum(axis=1), p @ v)
+
+
+def merge_states(x: State, y: State) -> State:
+    """The softmax merge of [ES] formula 2, read with its normalisers restored."""
+    m = np.maximum(x.m, y.m)
+    fx, fy = _factor(x.m, m), _factor(y.m, m)
+    return State(m, fx * x.l + fy * y.l, fx[:, None] * x.o + fy[:, None] * y.o)
+
+
+def finalize_state(st: State):
+    """O = O~ / l and LSE = m + ln l."""
+    return st.o / st.l[:, None], st.m + np.log(st.l)
+
+
+def online_blocked_ref(q, k, v, scale, bounds):
+    """Running online softmax over key blocks, for one head.
+
+    q (N, d), k (M, d), v (M, dv); ``bounds`` lists the block ends in order
+    (e.g. [3, 5, M]).  Follows the loop of [ES] "Detalles de Implementación"
+    (query rows fixed, key blocks visited in order, running max and sum) and
+    the online normaliser of [IT]: per block the max is raised, the old sum and
+    output are scaled by exp(m_old - m_new), and the block's exponentials are
+    added.  O~ stays unnormalised until the end.
+    """
+    q, k, v = _f64(q), _f64(k), _f64(v)
+    st = empty_state(q.shape[0], v.shape[1])
+    j0 = 0
+    for j1 in bounds:
+        s = scale * (q @ k[j0:j1].T)
+        m_new = np.maximum(st.m, s.max(axis=1))
+        alpha = _factor(st.m, m_new)
+        p = np.exp(s - m_new[:, None])
+        st = State(m_new, alpha * st.l + p.sum(axis=1), alpha[:, None] * st.o + p @ v[j0:j1])
+        j0 = j1
+    return finalize_state(st)

@@ -1,0 +1,8 @@
+"""FlashAttention forward for MI355X (gfx950): exact softmax(scale * Q K^T) V
+computed tile by tile with a running row max and normaliser.
+
+``forward`` and ``forward_into`` are thin ctypes bindings of the C-ABI
+library ``libfa.so`` (see include/fa.h); every step of the computation runs
+in its HIP kernels.  ``inputs`` builds the seeded synthetic workloads.
+"""
+from .fa import forward, forward_into, library_path, load_library  # noqa: F401

@@ -1,0 +1,82 @@
+"""ctypes binding of libfa.so (include/fa.h).  Argument marshalling only.
+
+torch tensors supply device memory and the current HIP stream; the library
+does every step of the attention computation in its own kernels.  There is no
+fallback: without the built library every call raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+
+import torch
+
+FA_DTYPE = {torch.float32: 0, torch.float16: 1, torch.bfloat16: 2}
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_LIB = None
+
+
+def library_path() -> str:
+    return os.path.join(_HERE, "libfa.so")
+
+
+def load_library():
+    """Load libfa.so once; raise if it has not been built."""
+    global _LIB
+    if _LIB is None:
+        path = library_path()
+        if not os.path.exists(path):
+            raise RuntimeError(f"{path} is missing: build it with __graft_entry__.build()")
+        lib = ctypes.CDLL(path)
+        lib.fa_forward.argtypes = [ctypes.c_void_p] * 5 + [ctypes.c_int64] * 4 + [
+            ctypes.c_float, ctypes.c_int, ctypes.c_void_p]
+        lib.fa_forward.restype = ctypes.c_int
+        lib.fa_status_string.argtypes = [ctypes.c_int]
+        lib.fa_status_string.restype = ctypes.c_char_p
+        lib.fa_version.argtypes = []
+        lib.fa_version.restype = ctypes.c_char_p
+        _LIB = lib
+    return _LIB
+
+
+def status_string(code: int) -> str:
+    return load_library().fa_status_string(int(code)).decode()
+
+
+def forward_into(q, k, v, o, lse, scale: float | None = None, stream=None) -> None:
+    """O and LSE are written in place; all five tensors are on one GPU."""
+    lib = load_library()
+    for name, t in (("q", q), ("k", k), ("v", v), ("o", o), ("lse", lse)):
+        if not t.is_cuda:
+            raise ValueError(f"{name} must be a GPU tensor")
+        if not t.is_contiguous():
+            raise ValueError(f"{name} must be contiguous (B, H, N, d) row-major")
+    if q.dtype not in FA_DTYPE or k.dtype != q.dtype or v.dtype != q.dtype or o.dtype != q.dtype:
+        raise ValueError(f"q, k, v, o must share one of {list(FA_DTYPE)}")
+    if lse.dtype != torch.float32:
+        raise ValueError("lse must be float32")
+    if q.dim() != 4 or k.shape != q.shape or v.shape != q.shape or o.shape != q.shape:
+        raise ValueError("q, k, v, o must all have shape (B, H, N, d)")
+    if tuple(lse.shape) != tuple(q.shape[:3]):
+        raise ValueError("lse must have shape (B, H, N)")
+    B, H, N, d = q.shape
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    if stream is None:
+        stream = torch.cuda.current_stream(q.device)
+    handle = stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
+    with torch.cuda.device(q.device):
+        rc = lib.fa_forward(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(),
+                            B, H, N, d, float(scale), FA_DTYPE[q.dtype], handle)
+    if rc != 0:
+        raise RuntimeError(f"fa_forward failed: {status_string(rc)} ({rc})")
+
+
+def forward(q, k, v, scale: float | None = None):
+    """Returns (O, LSE): O like q, LSE float32 (B, H, N), natural log."""
+    o = torch.empty_like(q)
+    lse = torch.empty(q.shape[:3], dtype=torch.float32, device=q.device)
+    forward_into(q, k, v, o, lse, scale)
+    return o, lse

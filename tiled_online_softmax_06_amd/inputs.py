@@ -1,0 +1,131 @@
+"""Seeded synthetic inputs for the attention forward workloads.
+
+This module is shared by the HIP path's tests/bench and by the oracle's tests.
+It holds none of the attention arithmetic: it only draws random numbers,
+rounds them to the storage dtype and names the workloads.
+
+Recipe (one line per workload, same order as the workload table):
+
+  id       B  H      N    d  dtype  Q, K                V          scale
+  tiny     1  1    256   64  fp32   N(0,1)              N(0,1)     1/sqrt(64)
+  ragged   4  8   1000   64  fp16   N(0,1)              N(0,1)     1/sqrt(64)
+  gpt2     8 12   1024   64  bf16   N(0,1)              N(0,1)     1/sqrt(64)
+  long     2 16   8192  128  bf16   N(0,1)              N(0,1)     1/sqrt(128)
+  xlong    1  8  65536  128  bf16   N(0, sigma=3)       U(-1,1)    1/sqrt(128)
+
+Workload k (1-based, in the order above) uses ``numpy.random.default_rng(1000+k)``
+and draws Q, then K, then V as float32 arrays of shape (B, H, N, d); the
+float32 draws are rounded to the storage dtype with round-to-nearest-even
+(torch's CPU ``Tensor.to``).  The same rounded values go to the GPU and,
+upcast exactly to float64, to the oracle.  The "xlong" workload is checked on
+256 distinct flat (b, h, n) query indices drawn without replacement by
+``default_rng(2005)`` and sorted.
+"""
+from __future__ import annotations
+
+import dataclasses
+import hashlib
+import math
+
+import numpy as np
+import torch
+
+DTYPES = {"fp32": torch.float32, "fp16": torch.float16, "bf16": torch.bfloat16}
+
+
+@dataclasses.dataclass(frozen=True)
+class Workload:
+    name: str
+    index: int          # 1-based position in the workload table (seed = 1000 + index)
+    B: int
+    H: int
+    N: int
+    d: int
+    dtype: str          # "fp32" | "fp16" | "bf16"
+    qk_sigma: float = 1.0
+    v_dist: str = "normal"   # "normal" (sigma 1) or "uniform" (-1, 1)
+    sample_rows: int = 0     # 0: every query row is checked; else this many sampled rows
+
+    @property
+    def scale(self) -> float:
+        return 1.0 / math.sqrt(self.d)
+
+    @property
+    def seed(self) -> int:
+        return 1000 + self.index
+
+    @property
+    def flops(self) -> int:
+        return 4 * self.B * self.H * self.N * self.N * self.d
+
+    @property
+    def esize(self) -> int:
+        return 4 if self.dtype == "fp32" else 2
+
+    @property
+    def compulsory_bytes(self) -> int:
+        """Read Q, K, V once, write O once, write the fp32 log-sum-exp."""
+        return 4 * self.B * self.H * self.N * self.d * self.esize + 4 * self.B * self.H * self.N
+
+
+WORKLOADS = {
+    w.name: w
+    for w in (
+        Workload("tiny", 1, 1, 1, 256, 64, "fp32"),
+        Workload("ragged", 2, 4, 8, 1000, 64, "fp16"),
+        Workload("gpt2", 3, 8, 12, 1024, 64, "bf16"),
+        Workload("long", 4, 2, 16, 8192, 128, "bf16"),
+        Workload("xlong", 5, 1, 8, 65536, 128, "bf16", qk_sigma=3.0, v_dist="uniform",
+                 sample_rows=256),
+    )
+}
+
+
+def make_inputs(w: Workload, seed: int | None = None):
+    """Return (q, k, v) as contiguous CPU tensors in the workload's dtype."""
+    rng = np.random.default_rng(w.seed if seed is None else seed)
+    shape = (w.B, w.H, w.N, w.d)
+    q = rng.standard_normal(shape, dtype=np.float32)
+    if w.qk_sigma != 1.0:
+        q *= np.float32(w.qk_sigma)
+    k = rng.standard_normal(shape, dtype=np.float32)
+    if w.qk_sigma != 1.0:
+        k *= np.float32(w.qk_sigma)
+    if w.v_dist == "uniform":
+        v = rng.uniform(-1.0, 1.0, size=shape).astype(np.float32)
+    else:
+        v = rng.standard_normal(shape, dtype=np.float32)
+    dt = DTYPES[w.dtype]
+    return tuple(torch.from_numpy(x).to(dt).contiguous() for x in (q, k, v))
+
+
+def random_qkv(shape, dtype: str, seed: int, sigma: float = 1.0):
+    """Generic seeded (q, k, v) of any shape (B, H, N, d), N(0, sigma) each."""
+    rng = np.random.default_rng(seed)
+    out = []
+    for _ in range(3):
+        x = rng.standard_normal(shape, dtype=np.float32)
+        if sigma != 1.0:
+            x *= np.float32(sigma)
+        out.append(torch.from_numpy(x).to(DTYPES[dtype]).contiguous())
+    return tuple(out)
+
+
+def sample_rows(w: Workload, count: int | None = None, seed: int = 2005) -> np.ndarray:
+    """Sorted distinct flat (b, h, n) indices of the query rows to check."""
+    total = w.B * w.H * w.N
+    count = w.sample_rows if count is None else count
+    rng = np.random.default_rng(seed)
+    return np.sort(rng.choice(total, size=count, replace=False))
+
+
+def to_float64(t: torch.Tensor) -> np.ndarray:
+    """Exact upcast of a CPU tensor (fp32/fp16/bf16 are all subsets of fp64)."""
+    return t.detach().cpu().to(torch.float64).numpy()
+
+
+def digest(*tensors: torch.Tensor) -> str:
+    h = hashlib.sha256()
+    for t in tensors:
+        h.update(t.contiguous().view(torch.uint8).numpy().tobytes())
+    return h.hexdigest()
