@@ -1,0 +1,191 @@
+#!/usr/bin/env python3
+"""Attention forward benchmark on one MI355X.
+
+    python bench.py [--steps K] [--warmup W] [--workload long] [--no-cpu-baseline]
+
+One step = one fa_forward launch over the whole workload (every query row of
+every head) with Q, K, V, O and LSE already resident in HBM.  Prints one JSON
+line: TFLOP/s counted as 4*B*H*N^2*d (non-causal), the kernel's roofline
+against the MFMA peak, and the CPU oracle timed on a bounded sample of the
+same workload on this host's cores.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, HERE)
+
+METRIC = "attention fwd TFLOP/s (4·B·H·N²·d) bf16 at 1 GPU + % of MFMA peak"
+# MI355X published dense matrix peaks (TFLOP/s) and HBM bandwidth (GB/s).
+PEAK_TFLOPS = {"bf16": 2500.0, "fp16": 2500.0, "fp32": 157.3}
+PEAK_HBM_GBS = 8000.0
+KERNEL_SOURCE = os.path.join(HERE, "tiled_online_softmax_06_amd", "csrc", "flash_fwd.hip")
+
+
+def kernel_hash() -> str:
+    with open(KERNEL_SOURCE, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def traffic_record(workload: str):
+    """HBM bytes per launch from committed PMC counter runs, if they were taken
+    on the current kernel source; else None."""
+    path = os.path.join(HERE, "profiles", f"flash_fwd_{workload}_hbm_traffic.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        rec = json.load(f)
+    if rec.get("kernel_sha256_16") != kernel_hash():
+        return None
+    return rec
+
+
+def cpu_baseline(w, q, k, v, heads: int, chunk: int, workers: int, gpu_out=None):
+    """The oracle, untuned, on a bounded sample: the first `heads` heads of the
+    workload, every query row, split into row chunks over a thread pool with
+    one BLAS thread per worker."""
+    from concurrent.futures import ThreadPoolExecutor
+
+    import numpy as np
+    from threadpoolctl import threadpool_limits
+
+    import oracle
+    from tiled_online_softmax_06_amd import inputs
+
+    heads = min(heads, w.B * w.H)
+    q64, k64, v64 = (inputs.to_float64(t.reshape(1, w.B * w.H, w.N, w.d)[:, :heads]) for t in (q, k, v))
+    scale = float(np.float32(w.scale))
+    tasks = [(h, i0) for h in range(heads) for i0 in range(0, w.N, chunk)]
+
+    def job(t):
+        h, i0 = t
+        rows = np.arange(h * w.N + i0, h * w.N + min(i0 + chunk, w.N))
+        return rows, oracle.attention_ref(q64, k64, v64, scale, rows=rows)
+
+    with threadpool_limits(1):
+        t0 = time.perf_counter()
+        with ThreadPoolExecutor(max_workers=workers) as ex:
+            results = list(ex.map(job, tasks))
+        dt = time.perf_counter() - t0
+    flops = 4 * heads * w.N * w.N * w.d
+    out = {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": workers, "kind": "oracle",
+           "sample": f"first {heads} of {w.B * w.H} heads, all {w.N} query rows each "
+                     f"({flops / 1e9:.1f} GFLOP in float64; {len(tasks)} row chunks of {chunk})",
+           "seconds": round(dt, 3)}
+    if gpu_out is not None:
+        o_gpu, lse_gpu = gpu_out
+        o_gpu = o_gpu.reshape(-1, w.d)
+        lse_gpu = lse_gpu.reshape(-1)
+        eo = el = 0.0
+        for rows, (o_ref, lse_ref) in results:
+            eo = max(eo, float(np.abs(o_gpu[rows].double().numpy() - o_ref).max()))
+            el = max(el, float(np.abs(lse_gpu[rows].double().numpy() - lse_ref).max()))
+        out["sample_max_abs_err"] = {"O": eo, "LSE": el}
+    return out
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="long")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-heads", type=int, default=4)
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="also run a plain 512 MiB device copy (for HBM counter calibration)")
+    args = ap.parse_args()
+
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(f"bench.py runs on exactly one GPU (asked for --gpus {args.gpus}, WORLD_SIZE {world}); "
+              "this attention forward is a single-GPU kernel and no multi-GPU path is built.",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    from tiled_online_softmax_06_amd import fa, inputs
+
+    w = inputs.WORKLOADS[args.workload]
+    dev = torch.device("cuda:0")
+    q, k, v = inputs.make_inputs(w)
+    qd, kd, vd = (t.to(dev) for t in (q, k, v))
+    o = torch.empty_like(qd)
+    lse = torch.empty(qd.shape[:3], dtype=torch.float32, device=dev)
+    stream = torch.cuda.current_stream(dev)
+
+    def step():
+        fa.forward_into(qd, kd, vd, o, lse, w.scale, stream=stream)
+
+    if args.calibrate_copy:
+        src = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    start = torch.cuda.Event(enable_timing=True)
+    end = torch.cuda.Event(enable_timing=True)
+    start.record(stream)
+    for _ in range(args.steps):
+        step()
+    end.record(stream)
+    torch.cuda.synchronize()
+    ms = start.elapsed_time(end) / max(args.steps, 1)
+
+    flops = w.flops
+    tflops = flops / (ms * 1e-3) / 1e12
+    props = torch.cuda.get_device_properties(dev)
+    peak = PEAK_TFLOPS[w.dtype]
+    roof = {"bound": "mfma", "achieved": round(tflops, 2), "peak": peak, "unit": "TFLOP/s",
+            "frac": round(tflops / peak, 4), "traffic": None,
+            "kernel": f"flash_fwd_16<{w.dtype}, d={w.d}>" if w.dtype != "fp32" else f"flash_fwd_32<d={w.d}>",
+            "avg_launch_ms": round(ms, 5)}
+    rec = traffic_record(w.name)
+    if rec is not None:
+        roof["traffic"] = rec["hbm_bytes_per_launch"]
+        roof["traffic_note"] = rec.get("note", "")
+
+    result = {
+        "metric": METRIC,
+        "value": round(tflops, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": w.dtype,
+        "data": "synthetic (seeded iid normal inputs, see tiled_online_softmax_06_amd/inputs.py)",
+        "config": {"workload": f"{w.name}: B={w.B} H={w.H} N={w.N} d={w.d} {w.dtype}, non-causal, "
+                               f"scale=1/sqrt({w.d})",
+                   "B": w.B, "H": w.H, "N": w.N, "d": w.d, "causal": False},
+        "pct_of_mfma_peak": round(100 * tflops / peak, 2),
+        "roofline": roof,
+        "device": {"name": props.name, "cu": props.multi_processor_count,
+                   "gcn_arch": getattr(props, "gcnArchName", "")},
+        "kernel_sha256_16": kernel_hash(),
+    }
+    if not args.no_cpu_baseline:
+        workers = max(1, min(16, len(os.sched_getaffinity(0))))
+        chunk = 512 if w.N >= 4096 else max(64, w.N // 4)
+        result["cpu_baseline"] = cpu_baseline(w, q, k, v, args.cpu_heads, chunk, workers,
+                                              gpu_out=(o.cpu(), lse.cpu()))
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,98 @@
+/*
+ * fa.h — C ABI of libfa.so: exact attention forward (FlashAttention) on
+ * AMD Instinct MI355X (gfx950).
+ *
+ * The operation (unite.ai page "Atención Flash: Revolucionando la Eficiencia
+ * de los Modelos de Transformador": the standard-attention code block defines
+ * it; section "La Matemática detrás de la Atención Flash", formulas 1 and 2,
+ * and section "Detalles de Implementación" give the blocked evaluation with a
+ * running row maximum and running sum; nisoo.com page "Un'immersione
+ * approfondita nell'algoritmo FlashAttention – parte 3", sections "Softmax
+ * Sicura" and "SafeSoftmax con Calcolo Normalizzatore Online"):
+ *
+ *     for every (b, h) and query row i:
+ *       S_ij  = scale * <Q[b,h,i,:], K[b,h,j,:]>           j = 0 .. N-1
+ *       O[b,h,i,:] = sum_j exp(S_ij) V[b,h,j,:] / sum_j exp(S_ij)
+ *       LSE[b,h,i] = ln sum_j exp(S_ij)
+ *
+ * No causal or padding mask, no dropout.  The N x N matrix S is never
+ * written to memory: it is produced tile by tile on chip and folded into a
+ * running (max, sum, output) state per query row.
+ */
+#ifndef FA_H
+#define FA_H
+
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Element type of Q, K, V and O. */
+typedef enum {
+    FA_DTYPE_FP32 = 0,
+    FA_DTYPE_FP16 = 1,
+    FA_DTYPE_BF16 = 2
+} fa_dtype_t;
+
+/* Return codes of fa_forward. */
+typedef enum {
+    FA_OK = 0,
+    FA_ERR_NULL_POINTER = 1,          /* a tensor pointer is NULL while B*H*N > 0      */
+    FA_ERR_BAD_SHAPE = 2,             /* B, H, N or d negative, or sizes overflow       */
+    FA_ERR_UNSUPPORTED_HEAD_DIM = 3,  /* d is not 64 or 128                             */
+    FA_ERR_UNSUPPORTED_DTYPE = 4,     /* dtype is not one of fa_dtype_t                 */
+    FA_ERR_MISALIGNED = 5,            /* Q/K/V/O not 16-byte or LSE not 4-byte aligned  */
+    FA_ERR_ALIAS = 6,                 /* O or LSE overlaps an input or each other       */
+    FA_ERR_BAD_SCALE = 7,             /* scale is NaN or infinite                       */
+    FA_ERR_LAUNCH = 8                 /* the HIP kernel launch itself failed            */
+} fa_status_t;
+
+/*
+ * fa_forward — attention forward for a batch of heads.
+ *
+ * Q, K, V  device pointers, read only.  Dense row-major (B, H, N, d) tensors
+ *          of `dtype` (no strides; element [b,h,n,e] sits at
+ *          ((b*H + h)*N + n)*d + e).  They may alias each other.
+ * O        device pointer, written: (B, H, N, d), same dtype and layout.
+ * LSE      device pointer, written: (B, H, N) float32, the natural-log
+ *          log-sum-exp of row i of the *scaled* scores, ln sum_j exp(S_ij).
+ * B, H, N  batch, heads, sequence length (queries = keys = N).  N may be any
+ *          value >= 0; a partial last tile is masked, not padded by the caller.
+ * d        head dimension: 64 or 128.
+ * scale    multiplies Q.K^T before the softmax (usually 1/sqrt(d)); any finite
+ *          value.  It is applied to the float32 scores, never to the inputs.
+ * dtype    fa_dtype_t.  fp16/bf16: both products run on MFMA with float32
+ *          accumulation, and the softmax weights are rounded to `dtype` for the
+ *          second product.  fp32: both products use float32 MFMA.
+ * stream   HIP stream to launch on (0 = the null stream).  The call is
+ *          asynchronous: it returns after the launch; results are ready when
+ *          the stream reaches that point.
+ *
+ * Ownership: the caller owns every buffer.  The library allocates, frees,
+ * copies and synchronises nothing and keeps no state between calls
+ * (reentrant, thread safe).  Every element of O and LSE is written.
+ * Pointers must belong to the current HIP device.
+ *
+ * Errors: arguments are checked on the host before anything is launched;
+ * a failed check returns its code and touches no memory.  B*H*N == 0 returns
+ * FA_OK without a launch (pointers may then be NULL).  FA_ERR_LAUNCH reports a
+ * launch failure.  Faults during execution surface at the caller's next
+ * synchronisation, not here.
+ */
+int fa_forward(const void* Q, const void* K, const void* V, void* O, float* LSE,
+               int64_t B, int64_t H, int64_t N, int64_t d,
+               float scale, int dtype, hipStream_t stream);
+
+/* Static, human-readable name of a return code ("unknown status" otherwise). */
+const char* fa_status_string(int status);
+
+/* Static string naming the library build and its kernel tile configuration. */
+const char* fa_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FA_H */

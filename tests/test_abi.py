@@ -1,0 +1,105 @@
+"""The C-ABI library on the host: it loads, exports what include/fa.h declares,
+and rejects bad arguments before touching the GPU (no kernel is launched by
+any call in this file)."""
+import ctypes
+import math
+import os
+import re
+import subprocess
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "fa.h")
+
+
+@pytest.fixture(scope="module")
+def lib():
+    from tiled_online_softmax_06_amd import fa, build_lib
+    if not os.path.exists(fa.library_path()):
+        build_lib.build()
+    return fa.load_library()
+
+
+def _header_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return re.findall(r"^\s*(?:const\s+)?\w+\s*\*?\s*(fa_\w+)\s*\(", text, flags=re.M)
+
+
+def _header_enum(name):
+    text = open(HEADER).read()
+    body = re.search(r"typedef enum \{([^{}]*)\}\s*" + name, text).group(1)
+    body = re.sub(r"/\*.*?\*/", "", body, flags=re.S)
+    return {k: int(v) for k, v in re.findall(r"(FA_\w+)\s*=\s*(\d+)", body)}
+
+
+def test_exports_every_declared_function(lib):
+    funcs = _header_functions()
+    assert set(funcs) == {"fa_forward", "fa_status_string", "fa_version"}
+    out = subprocess.run(["nm", "-D", "--defined-only", lib._name], capture_output=True, text=True).stdout
+    exported = set(re.findall(r" T (\w+)$", out, flags=re.M))
+    for f in funcs:
+        assert f in exported, f"{f} not exported"
+        assert getattr(lib, f) is not None
+
+
+def test_binding_constants_match_header():
+    import torch
+    from tiled_online_softmax_06_amd import fa
+    dt = _header_enum("fa_dtype_t")
+    assert fa.FA_DTYPE == {torch.float32: dt["FA_DTYPE_FP32"], torch.float16: dt["FA_DTYPE_FP16"],
+                           torch.bfloat16: dt["FA_DTYPE_BF16"]}
+
+
+def test_status_strings(lib):
+    codes = _header_enum("fa_status_t")
+    seen = set()
+    for name, code in codes.items():
+        s = lib.fa_status_string(code).decode()
+        assert s and s != "unknown status", name
+        seen.add(s)
+    assert len(seen) == len(codes)
+    assert lib.fa_status_string(999).decode() == "unknown status"
+    assert "gfx950" in lib.fa_version().decode()
+
+
+# Fake, never dereferenced device addresses: every call below fails a check
+# before any HIP call, so nothing is read or written through them.
+A = 0x7F0000000000
+MB = 1 << 20
+
+
+def call(lib, q=A, k=A + 64 * MB, v=A + 128 * MB, o=A + 192 * MB, lse=A + 256 * MB,
+         B=1, H=1, N=128, d=64, scale=0.125, dtype=2):
+    return lib.fa_forward(q, k, v, o, lse, B, H, N, d, scale, dtype, None)
+
+
+def test_error_codes(lib):
+    codes = _header_enum("fa_status_t")
+    assert call(lib, B=-1) == codes["FA_ERR_BAD_SHAPE"]
+    assert call(lib, N=-5) == codes["FA_ERR_BAD_SHAPE"]
+    assert call(lib, d=-64) == codes["FA_ERR_BAD_SHAPE"]
+    assert call(lib, B=1 << 40, H=1 << 40) == codes["FA_ERR_BAD_SHAPE"]       # size overflow
+    assert call(lib, N=1 << 31) == codes["FA_ERR_BAD_SHAPE"]                  # 32-bit kernel index
+    assert call(lib, d=96) == codes["FA_ERR_UNSUPPORTED_HEAD_DIM"]
+    assert call(lib, d=256) == codes["FA_ERR_UNSUPPORTED_HEAD_DIM"]
+    assert call(lib, dtype=3) == codes["FA_ERR_UNSUPPORTED_DTYPE"]
+    assert call(lib, dtype=-1) == codes["FA_ERR_UNSUPPORTED_DTYPE"]
+    for bad in (math.nan, math.inf, -math.inf):
+        assert call(lib, scale=bad) == codes["FA_ERR_BAD_SCALE"]
+    for field in ("q", "k", "v", "o", "lse"):
+        assert call(lib, **{field: None}) == codes["FA_ERR_NULL_POINTER"], field
+    for field in ("q", "k", "v", "o"):
+        assert call(lib, **{field: A + 8}) == codes["FA_ERR_MISALIGNED"], field
+    assert call(lib, lse=A + 256 * MB + 2) == codes["FA_ERR_MISALIGNED"]
+    # outputs overlapping an input or each other
+    assert call(lib, o=A + 64) == codes["FA_ERR_ALIAS"]                       # O inside Q
+    assert call(lib, o=A + 128 * MB) == codes["FA_ERR_ALIAS"]                 # O == V
+    assert call(lib, lse=A + 192 * MB + 16) == codes["FA_ERR_ALIAS"]          # LSE inside O
+    assert call(lib, lse=A + 64 * MB + 16384 - 16) == codes["FA_ERR_ALIAS"]   # LSE tail in K
+
+
+def test_empty_problem_is_a_no_op(lib):
+    for shape in ({"B": 0}, {"H": 0}, {"N": 0}):
+        assert call(lib, q=None, k=None, v=None, o=None, lse=None, **shape) == 0

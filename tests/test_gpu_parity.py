@@ -1,0 +1,182 @@
+"""Parity of the HIP path (through the C ABI) with the float64 oracle.
+
+Bar: max-abs error on O <= 1e-4 (fp32 inputs) / 2e-2 (fp16, bf16 inputs),
+on LSE <= 1e-3, every output finite, every element written.
+"""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from tiled_online_softmax_06_amd import fa, inputs
+
+pytestmark = pytest.mark.gpu
+
+O_TOL = {"fp32": 1e-4, "fp16": 2e-2, "bf16": 2e-2}
+LSE_TOL = 1e-3
+DEV = "cuda:0"
+
+
+def f32(x):
+    return float(np.float32(x))
+
+
+def run(q, k, v, scale=None, stream=None):
+    """Upload, run through the C ABI into NaN-filled outputs, return CPU copies."""
+    qd, kd, vd = (t.to(DEV) for t in (q, k, v))
+    o = torch.full_like(qd, float("nan"))
+    lse = torch.full(qd.shape[:3], float("nan"), dtype=torch.float32, device=DEV)
+    fa.forward_into(qd, kd, vd, o, lse, scale, stream=stream)
+    torch.cuda.synchronize()
+    return o.cpu(), lse.cpu()
+
+
+def check(o, lse, ref_o, ref_lse, dtype, what):
+    o = o.to(torch.float64).numpy()
+    lse = lse.to(torch.float64).numpy()
+    assert np.isfinite(o).all(), f"{what}: non-finite O"
+    assert np.isfinite(lse).all(), f"{what}: non-finite LSE"
+    eo = float(np.abs(o - ref_o).max()) if o.size else 0.0
+    el = float(np.abs(lse - ref_lse).max()) if lse.size else 0.0
+    print(f"{what}: max|dO| {eo:.3e} max|dLSE| {el:.3e}", flush=True)
+    assert eo <= O_TOL[dtype], f"{what}: O error {eo:.3e} > {O_TOL[dtype]}"
+    assert el <= LSE_TOL, f"{what}: LSE error {el:.3e} > {LSE_TOL}"
+    return eo, el
+
+
+def oracle_full(q, k, v, scale):
+    return oracle.attention_ref(inputs.to_float64(q), inputs.to_float64(k), inputs.to_float64(v), f32(scale))
+
+
+@pytest.mark.parametrize("name", ["tiny", "ragged", "gpt2"])
+def test_workload_full(name):
+    """Every output element of the three small workloads against the oracle."""
+    w = inputs.WORKLOADS[name]
+    q, k, v = inputs.make_inputs(w)
+    o, lse = run(q, k, v, w.scale)
+    ref_o, ref_lse = oracle_full(q, k, v, w.scale)
+    check(o, lse, ref_o, ref_lse, w.dtype, name)
+
+
+@pytest.mark.parametrize("name,count", [("long", 2048), ("xlong", 256)])
+def test_workload_sampled_rows(name, count):
+    """Full-size workloads in the benchmark's launch configuration; the oracle
+    computes a seeded sample of rows one by one (xlong: its 256 rows)."""
+    w = inputs.WORKLOADS[name]
+    q, k, v = inputs.make_inputs(w)
+    o, lse = run(q, k, v, w.scale)
+    rows = inputs.sample_rows(w, count)
+    # always include the first and last row of every head boundary region
+    ref_o, ref_lse = oracle.attention_ref(inputs.to_float64(q), inputs.to_float64(k), inputs.to_float64(v),
+                                          f32(w.scale), rows=rows)
+    o_all = o.reshape(-1, w.d)
+    assert np.isfinite(o_all.to(torch.float64).numpy()).all(), "non-finite O somewhere"
+    assert np.isfinite(lse.numpy()).all(), "non-finite LSE somewhere"
+    check(o_all[rows], lse.reshape(-1)[rows], ref_o, ref_lse, w.dtype, name)
+
+
+RAGGED_N = [1, 2, 31, 63, 64, 65, 127, 128, 129, 200, 1000]
+
+
+@pytest.mark.parametrize("dtype", ["fp32", "fp16", "bf16"])
+@pytest.mark.parametrize("d", [64, 128])
+def test_ragged_lengths(dtype, d):
+    """Sequence lengths around the tile sizes, including N = 1."""
+    for n in RAGGED_N:
+        q, k, v = inputs.random_qkv((2, 3, n, d), dtype, seed=100 + n + d)
+        scale = 1.0 / math.sqrt(d)
+        o, lse = run(q, k, v, scale)
+        ref_o, ref_lse = oracle_full(q, k, v, scale)
+        check(o, lse, ref_o, ref_lse, dtype, f"{dtype} d={d} N={n}")
+
+
+@pytest.mark.parametrize("dtype", ["fp32", "bf16"])
+def test_single_key_gives_v(dtype):
+    """N = 1: O = V exactly representable, LSE = scale * q.k."""
+    q, k, v = inputs.random_qkv((3, 2, 1, 128), dtype, seed=5)
+    o, lse = run(q, k, v, 0.1)
+    assert torch.equal(o, v)
+    ref_lse = 0.1 * np.sum(inputs.to_float64(q) * inputs.to_float64(k), axis=-1)
+    assert np.abs(lse.double().numpy() - ref_lse).max() < 1e-3
+
+
+def test_identical_keys_give_mean_v():
+    """All keys equal: every weight is exactly 1/N, O = mean of V."""
+    n, d = 300, 64
+    q, _, v = inputs.random_qkv((1, 2, n, d), "bf16", seed=6)
+    k = q[:, :, :1].expand(1, 2, n, d).contiguous()
+    o, lse = run(q, k, v, 0.125)
+    mean_v = inputs.to_float64(v).mean(axis=2, keepdims=True)
+    assert np.abs(o.double().numpy() - mean_v).max() < 2e-2
+    ref_lse = 0.125 * np.sum(inputs.to_float64(q) * inputs.to_float64(k), axis=-1) + math.log(n)
+    assert np.abs(lse.double().numpy() - ref_lse).max() < 1e-3
+
+
+def test_identity_values_read_out_the_weights():
+    """V = I (N = d = 64, fp32): O is the softmax matrix; rows sum to 1."""
+    q, k, _ = inputs.random_qkv((1, 1, 64, 64), "fp32", seed=7)
+    v = torch.eye(64, dtype=torch.float32).reshape(1, 1, 64, 64).contiguous()
+    o, lse = run(q, k, v, 0.125)
+    ref_o, ref_lse = oracle_full(q, k, v, 0.125)
+    check(o, lse, ref_o, ref_lse, "fp32", "V=I")
+    assert np.abs(o.double().numpy().sum(-1) - 1).max() < 1e-5
+
+
+def test_key_shift_invariance_fp32():
+    """K + u (same u for every key) leaves O unchanged and shifts LSE by
+    scale * q.u (the max subtraction absorbs a per-row constant)."""
+    q, k, v = inputs.random_qkv((2, 2, 257, 64), "fp32", seed=8)
+    u = torch.from_numpy(np.random.default_rng(9).standard_normal(64).astype(np.float32) * 4)
+    o1, l1 = run(q, k, v, 0.125)
+    o2, l2 = run(q, (k + u).contiguous(), v, 0.125)
+    assert (o1 - o2).abs().max() < 1e-4
+    shift = 0.125 * (inputs.to_float64(q) @ u.double().numpy())
+    assert np.abs(l2.double().numpy() - l1.double().numpy() - shift).max() < 2e-3
+
+
+@pytest.mark.parametrize("scale", [0.0, -0.09, 0.6])
+def test_scales(scale):
+    """scale = 0 gives uniform weights; negative and large scales stay exact."""
+    q, k, v = inputs.random_qkv((2, 2, 200, 128), "bf16", seed=10)
+    o, lse = run(q, k, v, scale)
+    ref_o, ref_lse = oracle_full(q, k, v, scale)
+    check(o, lse, ref_o, ref_lse, "bf16", f"scale={scale}")
+
+
+def test_large_logits_rescaling():
+    """Logits with std ~ 9 and increasing row max along the keys (keys sorted by
+    q.k for one query) force repeated rescaling of the running state."""
+    q, k, v = inputs.random_qkv((1, 2, 1536, 128), "bf16", seed=11, sigma=3.0)
+    order = torch.argsort((k.float() @ q.float()[0, 0, 0]).reshape(2, -1)[0])
+    k = k[:, :, order].contiguous()
+    o, lse = run(q, k, v, 1 / math.sqrt(128))
+    ref_o, ref_lse = oracle_full(q, k, v, 1 / math.sqrt(128))
+    check(o, lse, ref_o, ref_lse, "bf16", "large logits")
+
+
+def test_deterministic():
+    """Two runs give bitwise equal outputs (no atomics, fixed reduction order)."""
+    w = inputs.WORKLOADS["gpt2"]
+    q, k, v = inputs.make_inputs(w)
+    o1, l1 = run(q, k, v, w.scale)
+    o2, l2 = run(q, k, v, w.scale)
+    assert torch.equal(o1, o2) and torch.equal(l1, l2)
+
+
+def test_side_stream():
+    """Launch on a non-default stream; results equal the default-stream run."""
+    q, k, v = inputs.random_qkv((2, 4, 640, 64), "fp16", seed=12)
+    o1, l1 = run(q, k, v, 0.125)
+    s = torch.cuda.Stream()
+    with torch.cuda.stream(s):
+        o2, l2 = run(q, k, v, 0.125, stream=s)
+    assert torch.equal(o1, o2) and torch.equal(l1, l2)
+
+
+def test_aliased_output_rejected_on_device():
+    q, k, v = (t.to(DEV) for t in inputs.random_qkv((1, 1, 64, 64), "bf16", seed=13))
+    lse = torch.empty((1, 1, 64), dtype=torch.float32, device=DEV)
+    with pytest.raises(RuntimeError, match="overlaps"):
+        fa.forward_into(q, k, v, q, lse)

@@ -1,0 +1,74 @@
+// fa_api.hip — the C ABI of include/fa.h: host-side argument checks and
+// dispatch to the gfx950 kernels.  No allocation, copy or synchronisation.
+#include <math.h>
+#include <stdint.h>
+#include <hip/hip_runtime.h>
+
+#include "fa_internal.h"
+#include "../../include/fa.h"
+
+namespace {
+
+bool overlaps(const void* a, int64_t abytes, const void* b, int64_t bbytes) {
+    const uintptr_t a0 = (uintptr_t)a, b0 = (uintptr_t)b;
+    return a0 < b0 + (uintptr_t)bbytes && b0 < a0 + (uintptr_t)abytes;
+}
+
+bool mul_ok(int64_t x, int64_t y, int64_t* out) {
+    if (x != 0 && y > INT64_MAX / x) return false;
+    *out = x * y;
+    return true;
+}
+
+}  // namespace
+
+extern "C" int fa_forward(const void* Q, const void* K, const void* V, void* O, float* LSE,
+                          int64_t B, int64_t H, int64_t N, int64_t d,
+                          float scale, int dtype, hipStream_t stream) {
+    if (B < 0 || H < 0 || N < 0 || d < 0) return FA_ERR_BAD_SHAPE;
+    if (dtype != FA_DTYPE_FP32 && dtype != FA_DTYPE_FP16 && dtype != FA_DTYPE_BF16)
+        return FA_ERR_UNSUPPORTED_DTYPE;
+    if (d != 64 && d != 128) return FA_ERR_UNSUPPORTED_HEAD_DIM;
+    if (!isfinite(scale)) return FA_ERR_BAD_SCALE;
+
+    int64_t bh = 0, rows = 0, elems = 0, bytes = 0;
+    if (!mul_ok(B, H, &bh) || !mul_ok(bh, N, &rows) || !mul_ok(rows, d, &elems) ||
+        !mul_ok(elems, dtype == FA_DTYPE_FP32 ? 4 : 2, &bytes))
+        return FA_ERR_BAD_SHAPE;
+    if (rows == 0) return FA_OK;
+    // Kernel index limits: N and the workgroup count are 32-bit.
+    if (N > INT32_MAX) return FA_ERR_BAD_SHAPE;
+    const int64_t tiles = bh * ((N + fa::kMinRowsPerWorkgroup - 1) / fa::kMinRowsPerWorkgroup);
+    if (tiles > INT32_MAX) return FA_ERR_BAD_SHAPE;
+
+    if (!Q || !K || !V || !O || !LSE) return FA_ERR_NULL_POINTER;
+    if (((uintptr_t)Q | (uintptr_t)K | (uintptr_t)V | (uintptr_t)O) & 15u) return FA_ERR_MISALIGNED;
+    if ((uintptr_t)LSE & 3u) return FA_ERR_MISALIGNED;
+    const int64_t lbytes = rows * 4;
+    if (overlaps(O, bytes, Q, bytes) || overlaps(O, bytes, K, bytes) || overlaps(O, bytes, V, bytes) ||
+        overlaps(LSE, lbytes, Q, bytes) || overlaps(LSE, lbytes, K, bytes) ||
+        overlaps(LSE, lbytes, V, bytes) || overlaps(LSE, lbytes, O, bytes))
+        return FA_ERR_ALIAS;
+
+    fa::FwdArgs a{Q, K, V, O, LSE, bh, N, (int)d, dtype, scale};
+    return fa::launch_forward(a, stream) == hipSuccess ? FA_OK : FA_ERR_LAUNCH;
+}
+
+extern "C" const char* fa_status_string(int status) {
+    switch (status) {
+        case FA_OK: return "ok";
+        case FA_ERR_NULL_POINTER: return "null pointer";
+        case FA_ERR_BAD_SHAPE: return "bad shape";
+        case FA_ERR_UNSUPPORTED_HEAD_DIM: return "unsupported head dimension (need 64 or 128)";
+        case FA_ERR_UNSUPPORTED_DTYPE: return "unsupported dtype";
+        case FA_ERR_MISALIGNED: return "misaligned pointer";
+        case FA_ERR_ALIAS: return "output overlaps an input or the other output";
+        case FA_ERR_BAD_SCALE: return "scale is not finite";
+        case FA_ERR_LAUNCH: return "kernel launch failed";
+        default: return "unknown status";
+    }
+}
+
+extern "C" const char* fa_version(void) {
+    return fa::kernel_config_string();
+}

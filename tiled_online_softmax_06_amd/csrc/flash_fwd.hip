@@ -1,0 +1,549 @@
+// flash_fwd.hip — attention forward kernels for gfx950 (CDNA4).
+//
+// Method: the unite.ai page "Atención Flash: Revolucionando la Eficiencia de
+// los Modelos de Transformador" (section "La Matemática detrás de la Atención
+// Flash", formulas 1-2: safe softmax and the merge of partial softmaxes;
+// section "Detalles de Implementación": query blocks outside, key/value blocks
+// inside, running max M and sum L) and the nisoo.com page "Un'immersione
+// approfondita nell'algoritmo FlashAttention – parte 3" (sections "Concetto di
+// Divisione in Blocchi", "Softmax Sicura", "SafeSoftmax con Calcolo
+// Normalizzatore Online").
+//
+// Work split.  One workgroup owns 32*NW query rows of one (b, h) head; each of
+// its NW waves owns 32 rows for the whole sweep over the keys, so the running
+// state (max, sum, output) never leaves registers.  Workgroups are numbered so
+// that the hardware's round-robin over the 8 XCDs hands each XCD a contiguous
+// run of tiles: the query tiles of one head then share that XCD's L2 copy of
+// the head's K and V.
+//
+// Per key/value tile of BC keys:
+//   1. K and V are read from HBM with 16-byte coalesced loads (issued one tile
+//      ahead, into registers) and written to LDS: K row-major, V transposed
+//      (dim-major), which is the operand order the second product needs.
+//   2. S^T = K Q^T on MFMA (32x32 outputs, fp32 accumulation).  Computing the
+//      transpose puts one query per lane (lanes l and l+32 share a query), so
+//      the row max and row sum are in-lane reductions plus one cross-half swap.
+//   3. Keys >= N in a ragged last tile are masked.
+//   4. Row max; the running reference max is raised (and the accumulators
+//      rescaled by exp(m_old - m_new)) only when the tile max exceeds it by
+//      more than 2^8 in weight, so the rescale is rare after the first tiles.
+//   5. p = exp2(s * c - m) with c = scale * log2(e): one FMA and one v_exp_f32
+//      per score.  Each lane keeps its own partial row sum.
+//   6. O^T += V^T P^T on MFMA; P goes straight from the accumulator registers
+//      into the B operand (rounded to the input type for fp16/bf16).
+// Epilogue: one cross-half sum of l, O = O~ / l, LSE = (m + log2 l) ln 2.
+//
+// MFMA register layouts used (v_mfma_f32_32x32x16_{bf16,f16}, 32x32x2_f32):
+//   A (32 x K): lane l supplies row l%32; B (K x 32): lane l supplies column
+//   l%32; the K positions a lane supplies depend on l/32 identically for A and
+//   B, so any pairing of the two is consistent.  D (32 x 32): lane l holds
+//   column l%32, register r holds row 8*(r/4) + 4*(l/32) + r%4.
+#include <hip/hip_runtime.h>
+#include <math.h>
+#include <stdint.h>
+
+#include "fa_internal.h"
+#include "../../include/fa.h"
+
+namespace fa {
+namespace {
+
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
+
+constexpr float kLn2 = 0.693147180559945309f;
+// The reference max is raised only when a tile max exceeds it by more than
+// this (log2 units): weights stay <= 2^8, well inside fp16/bf16/fp32 range.
+constexpr float kRescaleSlack = 8.0f;
+
+template <typename T> struct Mfma;
+
+template <> struct Mfma<__bf16> {
+    using frag = bf16x8;
+    static __device__ __forceinline__ f32x16 run(u32x4 a, u32x4 b, f32x16 c) {
+        return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(frag, a),
+                                                       __builtin_bit_cast(frag, b), c, 0, 0, 0);
+    }
+    static __device__ __forceinline__ u32x4 pack(const float* p) {
+        frag f;
+#pragma unroll
+        for (int t = 0; t < 8; ++t) f[t] = (__bf16)p[t];
+        return __builtin_bit_cast(u32x4, f);
+    }
+    static __device__ __forceinline__ u32x2 pack4(const float* p) {
+        __bf16 __attribute__((ext_vector_type(4))) f;
+#pragma unroll
+        for (int t = 0; t < 4; ++t) f[t] = (__bf16)p[t];
+        return __builtin_bit_cast(u32x2, f);
+    }
+};
+
+template <> struct Mfma<_Float16> {
+    using frag = f16x8;
+    static __device__ __forceinline__ f32x16 run(u32x4 a, u32x4 b, f32x16 c) {
+        return __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(frag, a),
+                                                      __builtin_bit_cast(frag, b), c, 0, 0, 0);
+    }
+    static __device__ __forceinline__ u32x4 pack(const float* p) {
+        frag f;
+#pragma unroll
+        for (int t = 0; t < 8; ++t) f[t] = (_Float16)p[t];
+        return __builtin_bit_cast(u32x4, f);
+    }
+    static __device__ __forceinline__ u32x2 pack4(const float* p) {
+        _Float16 __attribute__((ext_vector_type(4))) f;
+#pragma unroll
+        for (int t = 0; t < 4; ++t) f[t] = (_Float16)p[t];
+        return __builtin_bit_cast(u32x2, f);
+    }
+};
+
+// Sum / max of the values held by lanes l and l^32 (the two lane halves that
+// hold the same query).  permlane32_swap exchanges the halves of two copies;
+// combining both results gives every lane the pair's sum / max.
+__device__ __forceinline__ float pair_max(float x) {
+    auto p = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return fmaxf(__uint_as_float(p[0]), __uint_as_float(p[1]));
+}
+__device__ __forceinline__ float pair_sum(float x) {
+    auto p = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return __uint_as_float(p[0]) + __uint_as_float(p[1]);
+}
+
+// Workgroup id -> logical tile id.  Dispatch sends workgroup w to XCD w % 8;
+// this bijection gives XCD x the contiguous logical range
+// [x*per + min(x, rem), ... + per + (x < rem)).
+__device__ __forceinline__ int xcd_tile(int wg, int total) {
+    const int per = total >> 3, rem = total & 7;
+    const int x = wg & 7, slot = wg >> 3;
+    return x * per + min(x, rem) + slot;
+}
+
+// Key row held by accumulator register r in lane half `half` (D layout).
+__device__ __forceinline__ int acc_row(int r, int half) {
+    return 8 * (r >> 2) + 4 * half + (r & 3);
+}
+
+// ---------------------------------------------------------------------------
+// fp16 / bf16 kernel
+// ---------------------------------------------------------------------------
+template <typename T, int D, int BC, int NW>
+__global__ void __launch_bounds__(NW * 64)
+flash_fwd_16(const T* __restrict__ Q, const T* __restrict__ K, const T* __restrict__ V,
+             T* __restrict__ O, float* __restrict__ LSE,
+             int n, int qtiles, int total, float c, int negate)
+{
+    using M = Mfma<T>;
+    constexpr int NT = NW * 64;
+    constexpr int BR = 32 * NW;
+    constexpr int KSTR = D + 8;      // K row stride in LDS (elements): +16 bytes
+    constexpr int VSTR = BC + 4;     // transposed-V row stride (elements): +8 bytes
+    constexpr int KT = BC / 32;      // 32-key sub-tiles
+    constexpr int DT = D / 32;       // 32-wide output column blocks
+    constexpr int KC = D / 16;       // contraction chunks of Q.K^T
+    constexpr int KCHUNKS = BC * D / 8;          // 16-byte chunks of a K tile
+    constexpr int KPER = (KCHUNKS + NT - 1) / NT;
+    constexpr int VUNITS = (BC / 4) * (D / 8);   // (4 keys x 8 dims) units of a V tile
+    constexpr int VPER = (VUNITS + NT - 1) / NT;
+    static_assert(BC % 32 == 0 && D % 32 == 0, "tile shape");
+
+    __shared__ __attribute__((aligned(16))) T ks[BC * KSTR];
+    __shared__ __attribute__((aligned(16))) T vt[D * VSTR];
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = tid >> 6;
+    const int col = lane & 31;
+    const int half = lane >> 5;
+
+    const int tile = xcd_tile(blockIdx.x, total);
+    const int bh = tile / qtiles;
+    const int qt = tile - bh * qtiles;
+    const int64_t base = (int64_t)bh * n * D;
+    const T* __restrict__ Qh = Q + base;
+    const T* __restrict__ Kh = K + base;
+    const T* __restrict__ Vh = V + base;
+    const int qrow = qt * BR + wave * 32 + col;
+
+    // Q^T as the B operand: lane (col, half) holds Q[qrow][16*kc + 8*half + 0..7].
+    u32x4 qf[KC];
+#pragma unroll
+    for (int kc = 0; kc < KC; ++kc) {
+        qf[kc] = qrow < n ? *(const u32x4*)(Qh + (int64_t)qrow * D + 16 * kc + 8 * half) : u32x4(0u);
+        if (negate) qf[kc] ^= u32x4(0x80008000u);
+    }
+
+    f32x16 acc[DT];
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt) acc[dt] = f32x16(0.f);
+    float mref = -INFINITY;   // reference max (log2 units of scaled scores)
+    float lsum = 0.f;         // this lane's part of the row sum
+
+    u32x4 kreg[KPER];
+    u32x4 vreg[VPER][4];
+
+    auto gload = [&](int j0) {
+#pragma unroll
+        for (int i = 0; i < KPER; ++i) {
+            const int ch = tid + i * NT;
+            const int key = ch / (D / 8), part = ch % (D / 8);
+            const bool ok = (KCHUNKS % NT == 0 || ch < KCHUNKS) && j0 + key < n;
+            kreg[i] = ok ? *(const u32x4*)(Kh + (int64_t)(j0 + key) * D + 8 * part) : u32x4(0u);
+        }
+#pragma unroll
+        for (int i = 0; i < VPER; ++i) {
+            const int u = tid + i * NT;
+            const int kg = u / (D / 8), part = u % (D / 8);
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const bool ok = (VUNITS % NT == 0 || u < VUNITS) && j0 + 4 * kg + r < n;
+                vreg[i][r] = ok ? *(const u32x4*)(Vh + (int64_t)(j0 + 4 * kg + r) * D + 8 * part) : u32x4(0u);
+            }
+        }
+    };
+
+    auto lstore = [&]() {
+#pragma unroll
+        for (int i = 0; i < KPER; ++i) {
+            const int ch = tid + i * NT;
+            if (KCHUNKS % NT == 0 || ch < KCHUNKS) {
+                const int key = ch / (D / 8), part = ch % (D / 8);
+                *(u32x4*)&ks[key * KSTR + 8 * part] = kreg[i];
+            }
+        }
+#pragma unroll
+        for (int i = 0; i < VPER; ++i) {
+            const int u = tid + i * NT;
+            if (VUNITS % NT == 0 || u < VUNITS) {
+                const int kg = u / (D / 8), part = u % (D / 8);
+#pragma unroll
+                for (int e = 0; e < 8; ++e) {
+                    const int w = e >> 1;
+                    u32x2 out;
+                    if (e & 1) {
+                        out.x = (vreg[i][0][w] >> 16) | (vreg[i][1][w] & 0xffff0000u);
+                        out.y = (vreg[i][2][w] >> 16) | (vreg[i][3][w] & 0xffff0000u);
+                    } else {
+                        out.x = (vreg[i][0][w] & 0xffffu) | (vreg[i][1][w] << 16);
+                        out.y = (vreg[i][2][w] & 0xffffu) | (vreg[i][3][w] << 16);
+                    }
+                    *(u32x2*)&vt[(8 * part + e) * VSTR + 4 * kg] = out;
+                }
+            }
+        }
+    };
+
+    const int ntiles = (n + BC - 1) / BC;
+    gload(0);
+    for (int t = 0; t < ntiles; ++t) {
+        const int j0 = t * BC;
+        __syncthreads();              // every wave is done with the previous tile
+        lstore();
+        __syncthreads();              // the tile is visible to every wave
+        if (t + 1 < ntiles) gload(j0 + BC);
+
+        // S^T = K Q^T for this tile (raw scores, fp32).
+        f32x16 s[KT];
+#pragma unroll
+        for (int kt = 0; kt < KT; ++kt) {
+            s[kt] = f32x16(0.f);
+#pragma unroll
+            for (int kc = 0; kc < KC; ++kc) {
+                const u32x4 a = *(const u32x4*)&ks[(32 * kt + col) * KSTR + 16 * kc + 8 * half];
+                s[kt] = M::run(a, qf[kc], s[kt]);
+            }
+        }
+
+        const bool tail = j0 + BC > n;
+        if (tail) {
+#pragma unroll
+            for (int kt = 0; kt < KT; ++kt)
+#pragma unroll
+                for (int r = 0; r < 16; ++r)
+                    if (j0 + 32 * kt + acc_row(r, half) >= n) s[kt][r] = -INFINITY;
+        }
+
+        float mt = -INFINITY;
+#pragma unroll
+        for (int kt = 0; kt < KT; ++kt)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) mt = fmaxf(mt, s[kt][r]);
+        mt = pair_max(mt) * c;
+
+        if (__ballot(mt > mref + kRescaleSlack)) {
+            const float mnew = fmaxf(mref, mt);
+            const float alpha = __builtin_amdgcn_exp2f(mref - mnew);
+            lsum *= alpha;
+#pragma unroll
+            for (int dt = 0; dt < DT; ++dt) acc[dt] *= alpha;
+            mref = mnew;
+        }
+
+#pragma unroll
+        for (int kt = 0; kt < KT; ++kt)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) s[kt][r] = __builtin_amdgcn_exp2f(fmaf(s[kt][r], c, -mref));
+        if (tail) {
+#pragma unroll
+            for (int kt = 0; kt < KT; ++kt)
+#pragma unroll
+                for (int r = 0; r < 16; ++r)
+                    if (j0 + 32 * kt + acc_row(r, half) >= n) s[kt][r] = 0.f;
+        }
+#pragma unroll
+        for (int kt = 0; kt < KT; ++kt)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) lsum += s[kt][r];
+
+        // O^T += V^T P^T.  B operand = 8 weights of this lane (registers
+        // 8*c2..8*c2+7 = keys 16*c2 + {0..3, 8..11} + 4*half of the sub-tile);
+        // A operand = V at those same keys for dim 32*dt + col.
+#pragma unroll
+        for (int kt = 0; kt < KT; ++kt) {
+#pragma unroll
+            for (int c2 = 0; c2 < 2; ++c2) {
+                float pv[8];
+#pragma unroll
+                for (int e = 0; e < 8; ++e) pv[e] = s[kt][8 * c2 + e];
+                const u32x4 b = M::pack(pv);
+#pragma unroll
+                for (int dt = 0; dt < DT; ++dt) {
+                    const T* row = &vt[(32 * dt + col) * VSTR + 32 * kt + 16 * c2 + 4 * half];
+                    const u32x2 lo = *(const u32x2*)row;
+                    const u32x2 hi = *(const u32x2*)(row + 8);
+                    acc[dt] = M::run(u32x4{lo.x, lo.y, hi.x, hi.y}, b, acc[dt]);
+                }
+            }
+        }
+    }
+
+    const float ltot = pair_sum(lsum);
+    if (qrow < n) {
+        const float inv = 1.0f / ltot;
+        T* orow = O + base + (int64_t)qrow * D;
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+            for (int g = 0; g < 4; ++g) {
+                float ov[4];
+#pragma unroll
+                for (int e = 0; e < 4; ++e) ov[e] = acc[dt][4 * g + e] * inv;
+                *(u32x2*)(orow + 32 * dt + 8 * g + 4 * half) = M::pack4(ov);
+            }
+        if (half == 0) LSE[(int64_t)bh * n + qrow] = (mref + log2f(ltot)) * kLn2;
+    }
+}
+
+// ---------------------------------------------------------------------------
+// fp32 kernel: same structure on v_mfma_f32_32x32x2_f32 (one contraction
+// element per lane per instruction, so V needs no transpose in LDS).
+// ---------------------------------------------------------------------------
+template <int D, int BC, int NW>
+__global__ void __launch_bounds__(NW * 64)
+flash_fwd_32(const float* __restrict__ Q, const float* __restrict__ K, const float* __restrict__ V,
+             float* __restrict__ O, float* __restrict__ LSE,
+             int n, int qtiles, int total, float c, int negate)
+{
+    constexpr int NT = NW * 64;
+    constexpr int BR = 32 * NW;
+    constexpr int STR = D + 4;       // row stride of K and V in LDS (floats)
+    constexpr int KT = BC / 32;
+    constexpr int DT = D / 32;
+    constexpr int CHUNKS = BC * D / 4;           // 16-byte chunks of a K (or V) tile
+    constexpr int PER = (CHUNKS + NT - 1) / NT;
+
+    __shared__ __attribute__((aligned(16))) float ks[BC * STR];
+    __shared__ __attribute__((aligned(16))) float vs[BC * STR];
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = tid >> 6;
+    const int col = lane & 31;
+    const int half = lane >> 5;
+
+    const int tile = xcd_tile(blockIdx.x, total);
+    const int bh = tile / qtiles;
+    const int qt = tile - bh * qtiles;
+    const int64_t base = (int64_t)bh * n * D;
+    const float* __restrict__ Qh = Q + base;
+    const float* __restrict__ Kh = K + base;
+    const float* __restrict__ Vh = V + base;
+    const int qrow = qt * BR + wave * 32 + col;
+
+    // Q^T as the B operand: lane (col, half) holds Q[qrow][2*kc + half].
+    float qf[D / 2];
+#pragma unroll
+    for (int kc = 0; kc < D / 2; ++kc) {
+        const float x = qrow < n ? Qh[(int64_t)qrow * D + 2 * kc + half] : 0.f;
+        qf[kc] = negate ? -x : x;
+    }
+
+    f32x16 acc[DT];
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt) acc[dt] = f32x16(0.f);
+    float mref = -INFINITY;
+    float lsum = 0.f;
+
+    u32x4 kreg[PER], vreg[PER];
+    auto gload = [&](int j0) {
+#pragma unroll
+        for (int i = 0; i < PER; ++i) {
+            const int ch = tid + i * NT;
+            const int key = ch / (D / 4), part = ch % (D / 4);
+            const bool ok = (CHUNKS % NT == 0 || ch < CHUNKS) && j0 + key < n;
+            kreg[i] = ok ? *(const u32x4*)(Kh + (int64_t)(j0 + key) * D + 4 * part) : u32x4(0u);
+            vreg[i] = ok ? *(const u32x4*)(Vh + (int64_t)(j0 + key) * D + 4 * part) : u32x4(0u);
+        }
+    };
+    auto lstore = [&]() {
+#pragma unroll
+        for (int i = 0; i < PER; ++i) {
+            const int ch = tid + i * NT;
+            if (CHUNKS % NT == 0 || ch < CHUNKS) {
+                const int key = ch / (D / 4), part = ch % (D / 4);
+                *(u32x4*)&ks[key * STR + 4 * part] = kreg[i];
+                *(u32x4*)&vs[key * STR + 4 * part] = vreg[i];
+            }
+        }
+    };
+
+    const int ntiles = (n + BC - 1) / BC;
+    gload(0);
+    for (int t = 0; t < ntiles; ++t) {
+        const int j0 = t * BC;
+        __syncthreads();
+        lstore();
+        __syncthreads();
+        if (t + 1 < ntiles) gload(j0 + BC);
+
+        f32x16 s[KT];
+#pragma unroll
+        for (int kt = 0; kt < KT; ++kt) {
+            s[kt] = f32x16(0.f);
+#pragma unroll
+            for (int kc = 0; kc < D / 2; ++kc)
+                s[kt] = __builtin_amdgcn_mfma_f32_32x32x2f32(ks[(32 * kt + col) * STR + 2 * kc + half],
+                                                             qf[kc], s[kt], 0, 0, 0);
+        }
+
+        const bool tail = j0 + BC > n;
+        if (tail) {
+#pragma unroll
+            for (int kt = 0; kt < KT; ++kt)
+#pragma unroll
+                for (int r = 0; r < 16; ++r)
+                    if (j0 + 32 * kt + acc_row(r, half) >= n) s[kt][r] = -INFINITY;
+        }
+        float mt = -INFINITY;
+#pragma unroll
+        for (int kt = 0; kt < KT; ++kt)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) mt = fmaxf(mt, s[kt][r]);
+        mt = pair_max(mt) * c;
+        if (__ballot(mt > mref + kRescaleSlack)) {
+            const float mnew = fmaxf(mref, mt);
+            const float alpha = __builtin_amdgcn_exp2f(mref - mnew);
+            lsum *= alpha;
+#pragma unroll
+            for (int dt = 0; dt < DT; ++dt) acc[dt] *= alpha;
+            mref = mnew;
+        }
+#pragma unroll
+        for (int kt = 0; kt < KT; ++kt)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) s[kt][r] = __builtin_amdgcn_exp2f(fmaf(s[kt][r], c, -mref));
+        if (tail) {
+#pragma unroll
+            for (int kt = 0; kt < KT; ++kt)
+#pragma unroll
+                for (int r = 0; r < 16; ++r)
+                    if (j0 + 32 * kt + acc_row(r, half) >= n) s[kt][r] = 0.f;
+        }
+#pragma unroll
+        for (int kt = 0; kt < KT; ++kt)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) lsum += s[kt][r];
+
+        // O^T += V^T P^T, one key per lane half per instruction: register r
+        // of this lane is key 32*kt + acc_row(r, half).
+#pragma unroll
+        for (int kt = 0; kt < KT; ++kt)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                const float* vrow = &vs[(32 * kt + acc_row(r, half)) * STR + col];
+#pragma unroll
+                for (int dt = 0; dt < DT; ++dt)
+                    acc[dt] = __builtin_amdgcn_mfma_f32_32x32x2f32(vrow[32 * dt], s[kt][r], acc[dt], 0, 0, 0);
+            }
+    }
+
+    const float ltot = pair_sum(lsum);
+    if (qrow < n) {
+        const float inv = 1.0f / ltot;
+        float* orow = O + base + (int64_t)qrow * D;
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+            for (int g = 0; g < 4; ++g) {
+                float4 ov;
+                ov.x = acc[dt][4 * g + 0] * inv;
+                ov.y = acc[dt][4 * g + 1] * inv;
+                ov.z = acc[dt][4 * g + 2] * inv;
+                ov.w = acc[dt][4 * g + 3] * inv;
+                *(float4*)(orow + 32 * dt + 8 * g + 4 * half) = ov;
+            }
+        if (half == 0) LSE[(int64_t)bh * n + qrow] = (mref + log2f(ltot)) * kLn2;
+    }
+}
+
+template <typename Kern, typename T>
+hipError_t launch(Kern kern, int nw, int br, const FwdArgs& a, hipStream_t stream) {
+    const int n = (int)a.n;
+    const int qtiles = (int)((a.n + br - 1) / br);
+    const int total = (int)(a.bh * qtiles);
+    const float c = fabsf(a.scale) * 1.4426950408889634f;
+    const int negate = a.scale < 0.f ? 1 : 0;
+    const T* q = (const T*)a.q;
+    const T* k = (const T*)a.k;
+    const T* v = (const T*)a.v;
+    T* o = (T*)a.o;
+    float* lse = a.lse;
+    void* args[] = {&q, &k, &v, &o, &lse, (void*)&n, (void*)&qtiles, (void*)&total, (void*)&c, (void*)&negate};
+    return hipLaunchKernel((const void*)kern, dim3(total), dim3(nw * 64), args, 0, stream);
+}
+
+}  // namespace
+
+hipError_t launch_forward(const FwdArgs& a, hipStream_t stream) {
+    constexpr int NW = 4;
+    constexpr int BR = 32 * NW;
+    switch (a.dtype) {
+        case FA_DTYPE_BF16:
+            return a.d == 128 ? launch<decltype(&flash_fwd_16<__bf16, 128, 64, NW>), __bf16>(
+                                    &flash_fwd_16<__bf16, 128, 64, NW>, NW, BR, a, stream)
+                              : launch<decltype(&flash_fwd_16<__bf16, 64, 64, NW>), __bf16>(
+                                    &flash_fwd_16<__bf16, 64, 64, NW>, NW, BR, a, stream);
+        case FA_DTYPE_FP16:
+            return a.d == 128 ? launch<decltype(&flash_fwd_16<_Float16, 128, 64, NW>), _Float16>(
+                                    &flash_fwd_16<_Float16, 128, 64, NW>, NW, BR, a, stream)
+                              : launch<decltype(&flash_fwd_16<_Float16, 64, 64, NW>), _Float16>(
+                                    &flash_fwd_16<_Float16, 64, 64, NW>, NW, BR, a, stream);
+        case FA_DTYPE_FP32:
+            return a.d == 128 ? launch<decltype(&flash_fwd_32<128, 32, NW>), float>(
+                                    &flash_fwd_32<128, 32, NW>, NW, BR, a, stream)
+                              : launch<decltype(&flash_fwd_32<64, 64, NW>), float>(
+                                    &flash_fwd_32<64, 64, NW>, NW, BR, a, stream);
+        default:
+            return hipErrorInvalidValue;
+    }
+}
+
+const char* kernel_config_string() {
+    return "flash_fwd gfx950: 4 waves x 32 query rows per workgroup; key tile 64 (fp32 d128: 32); "
+           "MFMA 32x32x16 bf16/f16, 32x32x2 f32; K row-major + V transposed in LDS";
+}
+
+}  // namespace fa
