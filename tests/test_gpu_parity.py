@@ -67,8 +67,10 @@ def test_workload_sampled_rows(name, count):
     w = inputs.WORKLOADS[name]
     q, k, v = inputs.make_inputs(w)
     o, lse = run(q, k, v, w.scale)
-    rows = inputs.sample_rows(w, count)
-    # always include the first and last row of every head boundary region
+    # seeded sample plus the tile-boundary rows of every head
+    edges = np.array([0, 31, 32, 127, 128, 255, 256, w.N - 1])
+    heads = np.arange(w.B * w.H)[:, None] * w.N
+    rows = np.union1d(inputs.sample_rows(w, count), (heads + edges).ravel())
     ref_o, ref_lse = oracle.attention_ref(inputs.to_float64(q), inputs.to_float64(k), inputs.to_float64(v),
                                           f32(w.scale), rows=rows)
     o_all = o.reshape(-1, w.d)
@@ -94,10 +96,15 @@ def test_ragged_lengths(dtype, d):
 
 @pytest.mark.parametrize("dtype", ["fp32", "bf16"])
 def test_single_key_gives_v(dtype):
-    """N = 1: O = V exactly representable, LSE = scale * q.k."""
+    """N = 1: the only weight is 1, so O = V and LSE = scale * q.k.  bf16
+    output is exact; fp32 is within a few ulp (the weight exp2(s*c - m) is 1 up
+    to the rounding of s*c)."""
     q, k, v = inputs.random_qkv((3, 2, 1, 128), dtype, seed=5)
     o, lse = run(q, k, v, 0.1)
-    assert torch.equal(o, v)
+    if dtype == "bf16":
+        assert torch.equal(o, v)
+    else:
+        assert ((o - v).abs() <= 1e-6 * v.abs().clamp(min=1.0)).all()
     ref_lse = 0.1 * np.sum(inputs.to_float64(q) * inputs.to_float64(k), axis=-1)
     assert np.abs(lse.double().numpy() - ref_lse).max() < 1e-3
 
@@ -146,9 +153,11 @@ def test_scales(scale):
 
 
 def test_large_logits_rescaling():
-    """Logits with std ~ 9 and increasing row max along the keys (keys sorted by
-    q.k for one query) force repeated rescaling of the running state."""
-    q, k, v = inputs.random_qkv((1, 2, 1536, 128), "bf16", seed=11, sigma=3.0)
+    """Logits with std ~ 9 (Q, K ~ N(0, 3), V ~ N(0, 1)) and increasing row
+    max along the keys (keys sorted by q.k for one query) force repeated
+    rescaling of the running state."""
+    q, k, _ = inputs.random_qkv((1, 2, 1536, 128), "bf16", seed=11, sigma=3.0)
+    _, _, v = inputs.random_qkv((1, 2, 1536, 128), "bf16", seed=12)
     order = torch.argsort((k.float() @ q.float()[0, 0, 0]).reshape(2, -1)[0])
     k = k[:, :, order].contiguous()
     o, lse = run(q, k, v, 1 / math.sqrt(128))
