@@ -130,32 +130,62 @@ __device__ __forceinline__ int acc_row(int r, int half) {
 // ---------------------------------------------------------------------------
 // fp16 / bf16 kernel
 // ---------------------------------------------------------------------------
+
+// LDS swizzles.  A K or V tile is stored row-major (key rows of D elements),
+// each row split into 16-byte chunks; chunk c of row r sits at position
+// c ^ f(r).  The DMA that fills LDS writes 1 KB per wave instruction
+// contiguously (64 lanes x 16 bytes), so the swizzle is applied by choosing
+// which global chunk each lane fetches.
+//  * K is read as the A operand of S^T = K Q^T: 16 lanes read one chunk of 16
+//    consecutive rows, so f must separate 16 consecutive rows.
+//  * V is read with the LDS transpose read (ds_read_b64_tr_b16): 32 lanes read
+//    4 consecutive rows x 4 consecutive chunks, so f must separate rows mod 4.
+template <int D> __device__ __forceinline__ constexpr int swz_k(int r) {
+    return D == 128 ? (r & 15) : ((r >> 1) & 7);
+}
+template <int D> __device__ __forceinline__ constexpr int swz_v(int r) {
+    return D == 128 ? 4 * (r & 3) : 4 * ((r >> 1) & 1);
+}
+
+template <int N_> struct Int { static constexpr int value = N_; };
+
+// 16-byte DMA from a buffer into LDS: lane l writes lds + 16*l (lds must be
+// wave-uniform).  The builtin only exists in the device pass; the host pass
+// must still see a body to emit the kernel's launch stub.
+__device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t rs, char* lds, int voff, int soff) {
+#if defined(__HIP_DEVICE_COMPILE__)
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (__attribute__((address_space(3))) void*)lds, 16, voff, soff, 0, 0);
+#endif
+}
+
 template <typename T, int D, int BC, int NW>
-__global__ void __launch_bounds__(NW * 64)
+__global__ void __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2)))
 flash_fwd_16(const T* __restrict__ Q, const T* __restrict__ K, const T* __restrict__ V,
              T* __restrict__ O, float* __restrict__ LSE,
              int n, int qtiles, int total, float c, int negate)
 {
     using M = Mfma<T>;
-    constexpr int NT = NW * 64;
     constexpr int BR = 32 * NW;
-    constexpr int KSTR = D + 8;      // K row stride in LDS (elements): +16 bytes
-    constexpr int VSTR = BC + 4;     // transposed-V row stride (elements): +8 bytes
-    constexpr int KT = BC / 32;      // 32-key sub-tiles
-    constexpr int DT = D / 32;       // 32-wide output column blocks
-    constexpr int KC = D / 16;       // contraction chunks of Q.K^T
-    constexpr int KCHUNKS = BC * D / 8;          // 16-byte chunks of a K tile
-    constexpr int KPER = (KCHUNKS + NT - 1) / NT;
-    constexpr int VUNITS = (BC / 4) * (D / 8);   // (4 keys x 8 dims) units of a V tile
-    constexpr int VPER = (VUNITS + NT - 1) / NT;
-    static_assert(BC % 32 == 0 && D % 32 == 0, "tile shape");
+    constexpr int ROWB = D * 2;              // bytes per K/V row
+    constexpr int CPR = D / 8;               // 16-byte chunks per row
+    constexpr int RPU = 64 / CPR;            // rows per 1 KB DMA unit
+    constexpr int TILEB = BC * ROWB;         // bytes of one K (or V) tile
+    constexpr int UNITS = TILEB / 1024;      // DMA units per tile
+    constexpr int UPW = UNITS / NW;          // DMA units per wave
+    constexpr int KT = BC / 32;              // 32-key sub-tiles
+    constexpr int DT = D / 32;               // 32-wide output column blocks
+    constexpr int KC = D / 16;               // contraction chunks of Q.K^T
+    static_assert(UNITS % NW == 0 && BC % 32 == 0, "tile shape");
 
-    __shared__ __attribute__((aligned(16))) T ks[BC * KSTR];
-    __shared__ __attribute__((aligned(16))) T vt[D * VSTR];
+    // Separate objects per stage and operand, so the compiler can see that the
+    // DMA into one stage never aliases the reads of the other.
+    __shared__ __attribute__((aligned(1024))) char ks0[TILEB];
+    __shared__ __attribute__((aligned(1024))) char vs0[TILEB];
+    __shared__ __attribute__((aligned(1024))) char ks1[TILEB];
+    __shared__ __attribute__((aligned(1024))) char vs1[TILEB];
 
-    const int tid = threadIdx.x;
-    const int lane = tid & 63;
-    const int wave = tid >> 6;
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int col = lane & 31;
     const int half = lane >> 5;
 
@@ -163,17 +193,73 @@ flash_fwd_16(const T* __restrict__ Q, const T* __restrict__ K, const T* __restri
     const int bh = tile / qtiles;
     const int qt = tile - bh * qtiles;
     const int64_t base = (int64_t)bh * n * D;
-    const T* __restrict__ Qh = Q + base;
-    const T* __restrict__ Kh = K + base;
-    const T* __restrict__ Vh = V + base;
     const int qrow = qt * BR + wave * 32 + col;
 
-    // Q^T as the B operand: lane (col, half) holds Q[qrow][16*kc + 8*half + 0..7].
+    // Q^T as the B operand: lane (col, half) holds Q[qrow][16*kc + 8*half + 0..7]
+    // (rows past the end are clamped: computed, never stored).
     u32x4 qf[KC];
+    {
+        const T* qp = Q + base + (int64_t)min(qrow, n - 1) * D + 8 * half;
 #pragma unroll
-    for (int kc = 0; kc < KC; ++kc) {
-        qf[kc] = qrow < n ? *(const u32x4*)(Qh + (int64_t)qrow * D + 16 * kc + 8 * half) : u32x4(0u);
-        if (negate) qf[kc] ^= u32x4(0x80008000u);
+        for (int kc = 0; kc < KC; ++kc) {
+            qf[kc] = *(const u32x4*)(qp + 16 * kc);
+            if (negate) qf[kc] ^= u32x4(0x80008000u);
+        }
+    }
+
+    // Per-head buffer resources: any offset past the head reads zero instead
+    // of faulting (the tail below also clamps, so this is a safety net).
+    const __amdgpu_buffer_rsrc_t krs =
+        __builtin_amdgcn_make_buffer_rsrc((void*)(K + base), (short)0, n * ROWB, 0x00020000);
+    const __amdgpu_buffer_rsrc_t vrs =
+        __builtin_amdgcn_make_buffer_rsrc((void*)(V + base), (short)0, n * ROWB, 0x00020000);
+
+    // DMA source offsets of this lane for the wave's units (within a tile).
+    const int lrow = lane / CPR;             // row inside a unit
+    const int lch = lane % CPR;              // LDS chunk position inside the row
+    int kvo[UPW], vvo[UPW];
+#pragma unroll
+    for (int i = 0; i < UPW; ++i) {
+        const int r = (wave * UPW + i) * RPU + lrow;
+        kvo[i] = r * ROWB + 16 * (lch ^ swz_k<D>(r));
+        vvo[i] = r * ROWB + 16 * (lch ^ swz_v<D>(r));
+    }
+
+    auto issue_loads = [&](int j0, auto stage) {
+        constexpr int st = decltype(stage)::value;
+        char* kdst = (st ? ks1 : ks0) + wave * UPW * 1024;
+        char* vdst = (st ? vs1 : vs0) + wave * UPW * 1024;
+        if (j0 + BC <= n) {
+#pragma unroll
+            for (int i = 0; i < UPW; ++i) {
+                dma16(krs, kdst + i * 1024, kvo[i], j0 * ROWB);
+                dma16(vrs, vdst + i * 1024, vvo[i], j0 * ROWB);
+            }
+        } else {
+            // Ragged last tile: rows past the end re-read the last row (finite
+            // values; their scores are masked and their weights are zero).
+#pragma unroll
+            for (int i = 0; i < UPW; ++i) {
+                const int r = (wave * UPW + i) * RPU + lrow;
+                const int g = min(j0 + r, n - 1) * ROWB;
+                dma16(krs, kdst + i * 1024, g + 16 * (lch ^ swz_k<D>(r)), 0);
+                dma16(vrs, vdst + i * 1024, g + 16 * (lch ^ swz_v<D>(r)), 0);
+            }
+        }
+    };
+
+    // LDS read offsets of this lane (within a stage).
+    // K, A operand of S^T: row col (+32 kt), logical chunk 2 kc + half.
+    const int kx = half ^ swz_k<D>(col);
+    // V, transpose read: lane 4t+s of each 16-lane group addresses row t
+    // (+4 half) and the 4-element segment s of the group's 16 dims.
+    const int trt = (lane & 15) >> 2, trs = lane & 3, trg = (lane >> 4) & 1;
+    int voff[DT];
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt) {
+        const int r = 4 * half + trt;
+        const int ch = 4 * dt + 2 * trg + (trs >> 1);
+        voff[dt] = r * ROWB + 16 * (ch ^ swz_v<D>(r)) + 8 * (trs & 1);
     }
 
     f32x16 acc[DT];
@@ -182,77 +268,19 @@ flash_fwd_16(const T* __restrict__ Q, const T* __restrict__ K, const T* __restri
     float mref = -INFINITY;   // reference max (log2 units of scaled scores)
     float lsum = 0.f;         // this lane's part of the row sum
 
-    u32x4 kreg[KPER];
-    u32x4 vreg[VPER][4];
+    auto compute = [&](auto stage, int j0) {
+        constexpr int st = decltype(stage)::value;
+        const char* kb = st ? ks1 : ks0;
+        const char* vb = st ? vs1 : vs0;
 
-    auto gload = [&](int j0) {
-#pragma unroll
-        for (int i = 0; i < KPER; ++i) {
-            const int ch = tid + i * NT;
-            const int key = ch / (D / 8), part = ch % (D / 8);
-            const bool ok = (KCHUNKS % NT == 0 || ch < KCHUNKS) && j0 + key < n;
-            kreg[i] = ok ? *(const u32x4*)(Kh + (int64_t)(j0 + key) * D + 8 * part) : u32x4(0u);
-        }
-#pragma unroll
-        for (int i = 0; i < VPER; ++i) {
-            const int u = tid + i * NT;
-            const int kg = u / (D / 8), part = u % (D / 8);
-#pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const bool ok = (VUNITS % NT == 0 || u < VUNITS) && j0 + 4 * kg + r < n;
-                vreg[i][r] = ok ? *(const u32x4*)(Vh + (int64_t)(j0 + 4 * kg + r) * D + 8 * part) : u32x4(0u);
-            }
-        }
-    };
-
-    auto lstore = [&]() {
-#pragma unroll
-        for (int i = 0; i < KPER; ++i) {
-            const int ch = tid + i * NT;
-            if (KCHUNKS % NT == 0 || ch < KCHUNKS) {
-                const int key = ch / (D / 8), part = ch % (D / 8);
-                *(u32x4*)&ks[key * KSTR + 8 * part] = kreg[i];
-            }
-        }
-#pragma unroll
-        for (int i = 0; i < VPER; ++i) {
-            const int u = tid + i * NT;
-            if (VUNITS % NT == 0 || u < VUNITS) {
-                const int kg = u / (D / 8), part = u % (D / 8);
-#pragma unroll
-                for (int e = 0; e < 8; ++e) {
-                    const int w = e >> 1;
-                    u32x2 out;
-                    if (e & 1) {
-                        out.x = (vreg[i][0][w] >> 16) | (vreg[i][1][w] & 0xffff0000u);
-                        out.y = (vreg[i][2][w] >> 16) | (vreg[i][3][w] & 0xffff0000u);
-                    } else {
-                        out.x = (vreg[i][0][w] & 0xffffu) | (vreg[i][1][w] << 16);
-                        out.y = (vreg[i][2][w] & 0xffffu) | (vreg[i][3][w] << 16);
-                    }
-                    *(u32x2*)&vt[(8 * part + e) * VSTR + 4 * kg] = out;
-                }
-            }
-        }
-    };
-
-    const int ntiles = (n + BC - 1) / BC;
-    gload(0);
-    for (int t = 0; t < ntiles; ++t) {
-        const int j0 = t * BC;
-        __syncthreads();              // every wave is done with the previous tile
-        lstore();
-        __syncthreads();              // the tile is visible to every wave
-        if (t + 1 < ntiles) gload(j0 + BC);
-
-        // S^T = K Q^T for this tile (raw scores, fp32).
+        // S^T = K Q^T (raw scores, fp32).
         f32x16 s[KT];
 #pragma unroll
         for (int kt = 0; kt < KT; ++kt) {
             s[kt] = f32x16(0.f);
 #pragma unroll
             for (int kc = 0; kc < KC; ++kc) {
-                const u32x4 a = *(const u32x4*)&ks[(32 * kt + col) * KSTR + 16 * kc + 8 * half];
+                const u32x4 a = *(const u32x4*)(kb + (32 * kt + col) * ROWB + 16 * ((2 * kc) ^ kx));
                 s[kt] = M::run(a, qf[kc], s[kt]);
             }
         }
@@ -298,9 +326,10 @@ flash_fwd_16(const T* __restrict__ Q, const T* __restrict__ K, const T* __restri
 #pragma unroll
             for (int r = 0; r < 16; ++r) lsum += s[kt][r];
 
-        // O^T += V^T P^T.  B operand = 8 weights of this lane (registers
-        // 8*c2..8*c2+7 = keys 16*c2 + {0..3, 8..11} + 4*half of the sub-tile);
-        // A operand = V at those same keys for dim 32*dt + col.
+        // O^T += V^T P^T.  B operand: the lane's 8 weights of registers
+        // 8*c2 .. 8*c2+7 (keys 16*c2 + {0..3, 8..11} + 4*half of the sub-tile).
+        // A operand: V at the same keys for dim 32*dt + col, two transpose
+        // reads of 4 keys each.
 #pragma unroll
         for (int kt = 0; kt < KT; ++kt) {
 #pragma unroll
@@ -309,15 +338,34 @@ flash_fwd_16(const T* __restrict__ Q, const T* __restrict__ K, const T* __restri
 #pragma unroll
                 for (int e = 0; e < 8; ++e) pv[e] = s[kt][8 * c2 + e];
                 const u32x4 b = M::pack(pv);
+                const char* vrow = vb + (32 * kt + 16 * c2) * ROWB;
 #pragma unroll
                 for (int dt = 0; dt < DT; ++dt) {
-                    const T* row = &vt[(32 * dt + col) * VSTR + 32 * kt + 16 * c2 + 4 * half];
-                    const u32x2 lo = *(const u32x2*)row;
-                    const u32x2 hi = *(const u32x2*)(row + 8);
-                    acc[dt] = M::run(u32x4{lo.x, lo.y, hi.x, hi.y}, b, acc[dt]);
+                    typedef short s16x4 __attribute__((ext_vector_type(4)));
+                    typedef __attribute__((address_space(3))) s16x4* lds_s16x4;
+                    const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4)(vrow + voff[dt]));
+                    const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4)(vrow + 8 * ROWB + voff[dt]));
+                    const u32x2 l2 = __builtin_bit_cast(u32x2, lo), h2 = __builtin_bit_cast(u32x2, hi);
+                    acc[dt] = M::run(u32x4{l2.x, l2.y, h2.x, h2.y}, b, acc[dt]);
                 }
             }
         }
+    };
+
+    // Two LDS stages: while one is computed on, the DMA fills the other.
+    const int ntiles = (n + BC - 1) / BC;
+    issue_loads(0, Int<0>{});
+    for (int t = 0;;) {
+        __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0): this wave's DMA landed
+        __syncthreads();                      // ... every wave's; stage 1 is free
+        if (t + 1 < ntiles) issue_loads((t + 1) * BC, Int<1>{});
+        compute(Int<0>{}, t * BC);
+        if (++t == ntiles) break;
+        __builtin_amdgcn_s_waitcnt(0x0F70);
+        __syncthreads();
+        if (t + 1 < ntiles) issue_loads((t + 1) * BC, Int<0>{});
+        compute(Int<1>{}, t * BC);
+        if (++t == ntiles) break;
     }
 
     const float ltot = pair_sum(lsum);
