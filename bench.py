@@ -59,7 +59,7 @@ def cpu_baseline(w, q, k, v, heads: int, chunk: int, workers: int, gpu_out=None)
     import oracle
     from tiled_online_softmax_06_amd import inputs
 
-    heads = min(heads, w.B * w.H)
+    heads = w.B * w.H if heads <= 0 else min(heads, w.B * w.H)
     q64, k64, v64 = (inputs.to_float64(t.reshape(1, w.B * w.H, w.N, w.d)[:, :heads]) for t in (q, k, v))
     scale = float(np.float32(w.scale))
     tasks = [(h, i0) for h in range(heads) for i0 in range(0, w.N, chunk)]
@@ -98,7 +98,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="long")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-heads", type=int, default=4)
+    ap.add_argument("--cpu-heads", type=int, default=0,
+                    help="heads the CPU oracle computes in full (0: every head of the workload)")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="also run a plain 512 MiB device copy (for HBM counter calibration)")
     args = ap.parse_args()
