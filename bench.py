@@ -34,6 +34,13 @@ def kernel_hash() -> str:
         return hashlib.sha256(f.read()).hexdigest()[:16]
 
 
+def kernel_name(w) -> str:
+    """The kernel fa_forward dispatches for a workload's dtype and head size."""
+    if w.dtype == "fp32":
+        return f"flash_fwd_32<d={w.d}>"
+    return f"flash_fwd_pp<{w.dtype}, d=128>" if w.d == 128 else f"flash_fwd_16<{w.dtype}, d={w.d}>"
+
+
 def traffic_record(workload: str):
     """HBM bytes per launch from committed PMC counter runs, if they were taken
     on the current kernel source; else None."""
@@ -151,7 +158,7 @@ def main():
     peak = PEAK_TFLOPS[w.dtype]
     roof = {"bound": "mfma", "achieved": round(tflops, 2), "peak": peak, "unit": "TFLOP/s",
             "frac": round(tflops / peak, 4), "traffic": None,
-            "kernel": f"flash_fwd_16<{w.dtype}, d={w.d}>" if w.dtype != "fp32" else f"flash_fwd_32<d={w.d}>",
+            "kernel": kernel_name(w),
             "avg_launch_ms": round(ms, 5)}
     rec = traffic_record(w.name)
     if rec is not None:

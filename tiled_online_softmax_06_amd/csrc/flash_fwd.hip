@@ -9,29 +9,33 @@
 // Divisione in Blocchi", "Softmax Sicura", "SafeSoftmax con Calcolo
 // Normalizzatore Online").
 //
-// Work split.  One workgroup owns 32*NW query rows of one (b, h) head; each of
-// its NW waves owns 32 rows for the whole sweep over the keys, so the running
-// state (max, sum, output) never leaves registers.  Workgroups are numbered so
-// that the hardware's round-robin over the 8 XCDs hands each XCD a contiguous
-// run of tiles: the query tiles of one head then share that XCD's L2 copy of
-// the head's K and V.
-//
-// Per key/value tile of BC keys:
-//   1. K and V are read from HBM with 16-byte coalesced loads (issued one tile
-//      ahead, into registers) and written to LDS: K row-major, V transposed
-//      (dim-major), which is the operand order the second product needs.
+// Every kernel: a workgroup owns a tile of query rows of one (b, h) head; each
+// wave owns 32 rows (one query per lane pair) for the whole sweep over the
+// keys, so the running state (max, sum, output) never leaves registers.  Per
+// key/value tile:
+//   1. K and V tiles are DMA'd from global memory straight into LDS (16 bytes
+//      per lane, XOR-swizzled so the operand reads below are conflict free).
 //   2. S^T = K Q^T on MFMA (32x32 outputs, fp32 accumulation).  Computing the
-//      transpose puts one query per lane (lanes l and l+32 share a query), so
-//      the row max and row sum are in-lane reductions plus one cross-half swap.
+//      transpose puts one query per lane, so the row max and row sum are
+//      in-lane reductions plus one cross-half swap.
 //   3. Keys >= N in a ragged last tile are masked.
 //   4. Row max; the running reference max is raised (and the accumulators
 //      rescaled by exp(m_old - m_new)) only when the tile max exceeds it by
 //      more than 2^8 in weight, so the rescale is rare after the first tiles.
 //   5. p = exp2(s * c - m) with c = scale * log2(e): one FMA and one v_exp_f32
-//      per score.  Each lane keeps its own partial row sum.
+//      per score.
 //   6. O^T += V^T P^T on MFMA; P goes straight from the accumulator registers
-//      into the B operand (rounded to the input type for fp16/bf16).
-// Epilogue: one cross-half sum of l, O = O~ / l, LSE = (m + log2 l) ln 2.
+//      into the B operand (rounded to the input type for fp16/bf16), V^T is
+//      read with the LDS transpose read ds_read_b64_tr_b16.
+// Epilogue: O = O~ / l, LSE = (m + log2 l) ln 2.
+//
+// Kernels:
+//   flash_fwd_pp  fp16/bf16, d = 128: 8 waves in two groups that alternate
+//                 between the MFMA work and the softmax work of a tile, one
+//                 group per phase, so each SIMD overlaps the two (below).
+//   flash_fwd_16  fp16/bf16, d = 64: 4 waves, two workgroups per CU that the
+//                 hardware interleaves.
+//   flash_fwd_32  fp32 inputs on v_mfma_f32_32x32x2_f32.
 //
 // MFMA register layouts used (v_mfma_f32_32x32x16_{bf16,f16}, 32x32x2_f32):
 //   A (32 x K): lane l supplies row l%32; B (K x 32): lane l supplies column
@@ -39,6 +43,7 @@
 //   B, so any pairing of the two is consistent.  D (32 x 32): lane l holds
 //   column l%32, register r holds row 8*(r/4) + 4*(l/32) + r%4.
 #include <hip/hip_runtime.h>
+#include <float.h>
 #include <math.h>
 #include <stdint.h>
 
@@ -148,6 +153,14 @@ template <int D> __device__ __forceinline__ constexpr int swz_v(int r) {
 }
 
 template <int N_> struct Int { static constexpr int value = N_; };
+
+template <int B_, int E_, typename F>
+__device__ __forceinline__ void static_for(F&& f) {
+    if constexpr (B_ < E_) {
+        f(Int<B_>{});
+        static_for<B_ + 1, E_>(f);
+    }
+}
 
 // 16-byte DMA from a buffer into LDS: lane l writes lds + 16*l (lds must be
 // wave-uniform).  The builtin only exists in the device pass; the host pass
@@ -386,6 +399,316 @@ flash_fwd_16(const T* __restrict__ Q, const T* __restrict__ K, const T* __restri
 }
 
 // ---------------------------------------------------------------------------
+// Ping-pong kernel (fp16 / bf16): 8 waves = two groups of 4; waves w and w+4
+// share a SIMD.  Each wave owns 32 query rows; key/value tiles of 64 keys.
+// Every wave runs MFMA phase j (S_j = Q K_j^T, then O += P_{j-1} V_{j-1}),
+// a workgroup barrier, softmax phase j (tile j's scores into weights), a
+// barrier; group B runs one phase behind group A, so on every SIMD one wave
+// feeds the matrix core while the other computes exponentials.
+//
+// LDS holds two stages of K and of V (64 KiB at d = 128, all under the
+// 64 KiB immediate-offset range).  Group A loads V_j during its softmax phase
+// j (phase 2j+1; the stage held V_{j-2}, last read in phase 2j-1); group B
+// loads K_{j+2} during its softmax phase j (phase 2j+2; the stage held K_j,
+// last read in phase 2j+1).  Each wave waits for its own loads before the
+// barrier that ends the phase, so every tile is complete one phase before its
+// first reader.  The first K operands of the next MFMA phase are read into
+// registers at the end of each softmax phase.
+// ---------------------------------------------------------------------------
+template <typename T, int D>
+__global__ void __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2)))
+flash_fwd_pp(const T* __restrict__ Q, const T* __restrict__ K, const T* __restrict__ V,
+             T* __restrict__ O, float* __restrict__ LSE,
+             int n, int qtiles, int total, float c, int negate)
+{
+    using M = Mfma<T>;
+    constexpr int NW = 8;
+    constexpr int BC = 64;                   // keys per tile
+    constexpr int BR = 32 * NW;              // query rows per workgroup
+    constexpr int ROWB = D * 2;              // bytes per K/V row
+    constexpr int CPR = D / 8;               // 16-byte chunks per row
+    constexpr int RPU = 64 / CPR;            // rows per 1 KB DMA unit
+    constexpr int TILEB = BC * ROWB;         // bytes of one K (or V) tile
+    constexpr int UNITS = TILEB / 1024;      // DMA units per tile
+    constexpr int UPW = UNITS / 4;           // units per wave of the loading group
+    constexpr int KT = BC / 32;              // 32-key sub-tiles
+    constexpr int DT = D / 32;               // 32-wide output column blocks
+    constexpr int KC = D / 16;               // contraction chunks of Q.K^T
+    constexpr int PC = BC / 16;              // 16-key contraction chunks of P.V
+    constexpr int R = 4;                     // LDS operand reads in flight
+    static_assert(UNITS % 4 == 0 && 4 * TILEB <= 65536, "tile shape");
+
+    __shared__ __attribute__((aligned(1024))) char ks0[TILEB];
+    __shared__ __attribute__((aligned(1024))) char ks1[TILEB];
+    __shared__ __attribute__((aligned(1024))) char vs0[TILEB];
+    __shared__ __attribute__((aligned(1024))) char vs1[TILEB];
+
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int group = wave >> 2;
+    const int gw = wave & 3;                 // wave index inside its group
+    const int col = lane & 31;
+    const int half = lane >> 5;
+
+    const int tile = xcd_tile(blockIdx.x, total);
+    const int bh = tile / qtiles;
+    const int qt = tile - bh * qtiles;
+    const int64_t base = (int64_t)bh * n * D;
+    const int qrow = qt * BR + wave * 32 + col;
+
+    // Q^T as the B operand: lane (col, half) holds Q[qrow][16 kc + 8 half + 0..7];
+    // rows past the end are clamped (computed, never stored).
+    u32x4 qf[KC];
+    {
+        const T* qp = Q + base + (int64_t)min(qrow, n - 1) * D + 8 * half;
+#pragma unroll
+        for (int kc = 0; kc < KC; ++kc) {
+            qf[kc] = *(const u32x4*)(qp + 16 * kc);
+            if (negate) qf[kc] ^= u32x4(0x80008000u);
+        }
+    }
+
+    const __amdgpu_buffer_rsrc_t krs =
+        __builtin_amdgcn_make_buffer_rsrc((void*)(K + base), (short)0, n * ROWB, 0x00020000);
+    const __amdgpu_buffer_rsrc_t vrs =
+        __builtin_amdgcn_make_buffer_rsrc((void*)(V + base), (short)0, n * ROWB, 0x00020000);
+
+    // DMA: this wave moves units gw*UPW .. of a tile; K and V use their own
+    // swizzles (chosen by the global chunk each lane fetches).
+    const int lrow = lane / CPR;
+    const int lch = lane % CPR;
+    auto issue = [&](__amdgpu_buffer_rsrc_t rs, char* stage, int j0, auto isk) {
+        constexpr bool IK = decltype(isk)::value;
+        char* dst = stage + gw * UPW * 1024;
+        if (j0 + BC <= n) {
+#pragma unroll
+            for (int i = 0; i < UPW; ++i) {
+                const int r = (gw * UPW + i) * RPU + lrow;
+                const int sw = IK ? swz_k<D>(r) : swz_v<D>(r);
+                dma16(rs, dst + i * 1024, r * ROWB + 16 * (lch ^ sw), j0 * ROWB);
+            }
+        } else {
+            // ragged last tile: rows past the end re-read the last row
+#pragma unroll
+            for (int i = 0; i < UPW; ++i) {
+                const int r = (gw * UPW + i) * RPU + lrow;
+                const int sw = IK ? swz_k<D>(r) : swz_v<D>(r);
+                dma16(rs, dst + i * 1024, min(j0 + r, n - 1) * ROWB + 16 * (lch ^ sw), 0);
+            }
+        }
+    };
+
+    // LDS read offsets.  K, A operand of S^T: row col (+32 kt), logical chunk
+    // 2 kc + half.  V, transpose read: lane 4t+s of each 16-lane group
+    // addresses row t (+4 half) and the 4-element segment s of the group's 16
+    // dims.
+    const int kx = half ^ swz_k<D>(col);
+    const int trt = (lane & 15) >> 2, trs = lane & 3, trg = (lane >> 4) & 1;
+    int voff[DT];
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt) {
+        const int r = 4 * half + trt;
+        const int ch = 4 * dt + 2 * trg + (trs >> 1);
+        voff[dt] = r * ROWB + 16 * (ch ^ swz_v<D>(r)) + 8 * (trs & 1);
+    }
+
+    f32x16 acc[DT];
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt) acc[dt] = f32x16(0.f);
+    float mref = -INFINITY;   // reference max (log2 units of scaled scores)
+    float lsum = 0.f;         // this lane's part of the row sum
+    f32x16 s[KT];             // raw scores of the current tile
+    u32x4 p[PC];              // its packed weights (B operands of P.V)
+    u32x4 ring[R];            // A operands in flight
+
+    typedef short s16x4 __attribute__((ext_vector_type(4)));
+    typedef __attribute__((address_space(3))) s16x4* lds_s16x4;
+
+    // The MFMA phase as a fixed program: QK steps (kc, kt) first, one K read
+    // each; then PV steps (pc, dt), two V transpose reads each.  Reads run R
+    // steps ahead through `ring`; sched_barrier pins the order.
+    auto mphase = [&](const char* kb, const char* vb, auto has_qk, auto has_pv, auto filled) {
+        constexpr int NQK = decltype(has_qk)::value ? KC * KT : 0;
+        constexpr int NPV = decltype(has_pv)::value ? PC * DT : 0;
+        constexpr int NS = NQK + NPV;
+        auto read = [&](auto step) {
+            constexpr int i = decltype(step)::value;
+            if constexpr (i < NQK) {
+                constexpr int kc = i / KT, kt = i % KT;
+                ring[i % R] = *(const u32x4*)(kb + (32 * kt + col) * ROWB + 16 * ((2 * kc) ^ kx));
+            } else {
+                constexpr int pc = (i - NQK) / DT, dt = (i - NQK) % DT;
+                const char* vrow = vb + 16 * pc * ROWB;
+                const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4)(vrow + voff[dt]));
+                const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4)(vrow + 8 * ROWB + voff[dt]));
+                const u32x2 l2 = __builtin_bit_cast(u32x2, lo), h2 = __builtin_bit_cast(u32x2, hi);
+                ring[i % R] = u32x4{l2.x, l2.y, h2.x, h2.y};
+            }
+        };
+        auto mma = [&](auto step) {
+            constexpr int i = decltype(step)::value;
+            if constexpr (i < NQK) {
+                constexpr int kc = i / KT, kt = i % KT;
+                s[kt] = M::run(ring[i % R], qf[kc], kc == 0 ? f32x16(0.f) : s[kt]);
+            } else {
+                constexpr int pc = (i - NQK) / DT, dt = (i - NQK) % DT;
+                acc[dt] = M::run(ring[i % R], p[pc], acc[dt]);
+            }
+        };
+        if constexpr (!decltype(filled)::value) static_for<0, (R < NS ? R : NS)>([&](auto i) { read(i); });
+        static_for<0, NS>([&](auto i) {
+            constexpr int k = decltype(i)::value;
+            __builtin_amdgcn_sched_barrier(0);
+            mma(i);
+            if constexpr (k + R < NS) read(Int<k + R>{});
+        });
+        __builtin_amdgcn_sched_barrier(0);
+    };
+    // First R K operands of an MFMA phase, read ahead at the end of the
+    // preceding softmax phase.
+    auto prefetch = [&](const char* kb) {
+        static_for<0, R>([&](auto step) {
+            constexpr int i = decltype(step)::value;
+            constexpr int kc = i / KT, kt = i % KT;
+            ring[i] = *(const u32x4*)(kb + (32 * kt + col) * ROWB + 16 * ((2 * kc) ^ kx));
+        });
+    };
+
+    // Online softmax of one tile (in place on s, packed into p).  Keys past
+    // the end of a ragged last tile get score -inf, hence weight 0 (the host
+    // never passes c = 0, so -inf * c stays -inf).
+    auto softmax = [&](int j0) {
+        if (j0 + BC > n) {
+#pragma unroll
+            for (int kt = 0; kt < KT; ++kt) {
+                const int lim = n - j0 - 32 * kt - 4 * half;
+#pragma unroll
+                for (int r = 0; r < 16; ++r)
+                    if (8 * (r >> 2) + (r & 3) >= lim) s[kt][r] = -INFINITY;
+            }
+        }
+        float mp[4];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) mp[q] = fmaxf(s[q >> 1][8 * (q & 1)], s[q >> 1][8 * (q & 1) + 1]);
+#pragma unroll
+        for (int kt = 0; kt < KT; ++kt)
+#pragma unroll
+            for (int r = 2; r < 16; ++r) {
+                const int q = 2 * kt + (r >> 3);
+                if ((r & 7) >= 2) mp[q] = fmaxf(mp[q], s[kt][r]);
+            }
+        const float mt = pair_max(fmaxf(fmaxf(mp[0], mp[1]), fmaxf(mp[2], mp[3]))) * c;
+        if (__ballot(mt > mref + kRescaleSlack)) {
+            const float mnew = fmaxf(mref, mt);
+            const float alpha = __builtin_amdgcn_exp2f(mref - mnew);
+            lsum *= alpha;
+#pragma unroll
+            for (int dt = 0; dt < DT; ++dt) acc[dt] *= alpha;
+            mref = mnew;
+        }
+        float part[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int kt = 0; kt < KT; ++kt)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                const float e = __builtin_amdgcn_exp2f(fmaf(s[kt][r], c, -mref));
+                s[kt][r] = e;
+                part[r & 3] += e;
+            }
+        lsum += (part[0] + part[1]) + (part[2] + part[3]);
+#pragma unroll
+        for (int pc = 0; pc < PC; ++pc) {
+            float w[8];
+#pragma unroll
+            for (int e = 0; e < 8; ++e) w[e] = s[pc >> 1][8 * (pc & 1) + e];
+            p[pc] = M::pack(w);
+        }
+        // keep the whole softmax inside its phase
+#pragma unroll
+        for (int pc = 0; pc < PC; ++pc) asm volatile("" : "+v"(p[pc]));
+        asm volatile("" : "+v"(lsum), "+v"(mref));
+    };
+
+    auto phase_barrier = [&]() {
+        __builtin_amdgcn_sched_barrier(0);
+        asm volatile("" ::: "memory");
+        __builtin_amdgcn_s_barrier();
+        asm volatile("" ::: "memory");
+        __builtin_amdgcn_sched_barrier(0);
+    };
+
+    const int ntiles = (n + BC - 1) / BC;
+    // Phase pair j (P = j & 1 selects the LDS stages at compile time):
+    // MFMA phase j reads K_j from ks[P] and V_{j-1} from vs[1-P].
+    auto pair = [&](int j, auto par, auto has_qk, auto has_pv, auto pf) {
+        constexpr int P = decltype(par)::value;
+        char* kcur = P ? ks1 : ks0;
+        char* knxt = P ? ks0 : ks1;
+        char* vprv = P ? vs0 : vs1;
+        char* vcur = P ? vs1 : vs0;
+        mphase(kcur, vprv, has_qk, has_pv, has_qk);
+        phase_barrier();
+        if (group == 0) {
+            if (j < ntiles) issue(vrs, vcur, j * BC, Int<0>{});
+        } else {
+            if (j + 2 < ntiles) issue(krs, kcur, (j + 2) * BC, Int<1>{});
+        }
+        if constexpr (decltype(has_qk)::value) softmax(j * BC);
+        if constexpr (decltype(pf)::value) prefetch(knxt);
+        __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0): this wave's loads landed
+        phase_barrier();
+    };
+
+    using F = Int<0>;
+    using Tr = Int<1>;
+    if (group == 1) {
+        issue(krs, ks0, 0, Int<1>{});
+        if (ntiles > 1) issue(krs, ks1, BC, Int<1>{});
+    }
+    __builtin_amdgcn_s_waitcnt(0x0F70);
+    phase_barrier();
+    prefetch(ks0);
+    if (group == 1) phase_barrier();     // group B runs one phase behind
+    if (ntiles == 1) {
+        pair(0, Int<0>{}, Tr{}, F{}, F{});
+        pair(1, Int<1>{}, F{}, Tr{}, F{});
+    } else {
+        pair(0, Int<0>{}, Tr{}, F{}, Tr{});
+        int j = 1;
+        for (; j + 2 < ntiles; j += 2) {
+            pair(j, Int<1>{}, Tr{}, Tr{}, Tr{});
+            pair(j + 1, Int<0>{}, Tr{}, Tr{}, Tr{});
+        }
+        // j odd; j == ntiles - 2 or ntiles - 1
+        if (j == ntiles - 2) {
+            pair(j, Int<1>{}, Tr{}, Tr{}, Tr{});
+            pair(j + 1, Int<0>{}, Tr{}, Tr{}, F{});
+            pair(j + 2, Int<1>{}, F{}, Tr{}, F{});
+        } else {
+            pair(j, Int<1>{}, Tr{}, Tr{}, F{});
+            pair(j + 1, Int<0>{}, F{}, Tr{}, F{});
+        }
+    }
+    if (group == 0) phase_barrier();
+
+    const float ltot = pair_sum(lsum);
+    if (qrow < n) {
+        const float inv = 1.0f / ltot;
+        T* orow = O + base + (int64_t)qrow * D;
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+            for (int g = 0; g < 4; ++g) {
+                float ov[4];
+#pragma unroll
+                for (int e = 0; e < 4; ++e) ov[e] = acc[dt][4 * g + e] * inv;
+                *(u32x2*)(orow + 32 * dt + 8 * g + 4 * half) = M::pack4(ov);
+            }
+        if (half == 0) LSE[(int64_t)bh * n + qrow] = (mref + log2f(ltot)) * kLn2;
+    }
+}
+
+// ---------------------------------------------------------------------------
 // fp32 kernel: same structure on v_mfma_f32_32x32x2_f32 (one contraction
 // element per lane per instruction, so V needs no transpose in LDS).
 // ---------------------------------------------------------------------------
@@ -552,7 +875,11 @@ hipError_t launch(Kern kern, int nw, int br, const FwdArgs& a, hipStream_t strea
     const int n = (int)a.n;
     const int qtiles = (int)((a.n + br - 1) / br);
     const int total = (int)(a.bh * qtiles);
-    const float c = fabsf(a.scale) * 1.4426950408889634f;
+    // c = |scale| log2(e) (a negative scale negates Q instead).  scale = 0 is
+    // passed as the smallest normal float: every score times it is far below
+    // the rounding of exp2 near 0, so the weights are exactly 1 as for c = 0,
+    // while a masked score -inf times it stays -inf (times 0 it would be NaN).
+    const float c = a.scale == 0.f ? FLT_MIN : fabsf(a.scale) * 1.4426950408889634f;
     const int negate = a.scale < 0.f ? 1 : 0;
     const T* q = (const T*)a.q;
     const T* k = (const T*)a.k;
@@ -570,13 +897,13 @@ hipError_t launch_forward(const FwdArgs& a, hipStream_t stream) {
     constexpr int BR = 32 * NW;
     switch (a.dtype) {
         case FA_DTYPE_BF16:
-            return a.d == 128 ? launch<decltype(&flash_fwd_16<__bf16, 128, 64, NW>), __bf16>(
-                                    &flash_fwd_16<__bf16, 128, 64, NW>, NW, BR, a, stream)
+            return a.d == 128 ? launch<decltype(&flash_fwd_pp<__bf16, 128>), __bf16>(
+                                    &flash_fwd_pp<__bf16, 128>, 8, 256, a, stream)
                               : launch<decltype(&flash_fwd_16<__bf16, 64, 64, NW>), __bf16>(
                                     &flash_fwd_16<__bf16, 64, 64, NW>, NW, BR, a, stream);
         case FA_DTYPE_FP16:
-            return a.d == 128 ? launch<decltype(&flash_fwd_16<_Float16, 128, 64, NW>), _Float16>(
-                                    &flash_fwd_16<_Float16, 128, 64, NW>, NW, BR, a, stream)
+            return a.d == 128 ? launch<decltype(&flash_fwd_pp<_Float16, 128>), _Float16>(
+                                    &flash_fwd_pp<_Float16, 128>, 8, 256, a, stream)
                               : launch<decltype(&flash_fwd_16<_Float16, 64, 64, NW>), _Float16>(
                                     &flash_fwd_16<_Float16, 64, 64, NW>, NW, BR, a, stream);
         case FA_DTYPE_FP32:
@@ -590,8 +917,9 @@ hipError_t launch_forward(const FwdArgs& a, hipStream_t stream) {
 }
 
 const char* kernel_config_string() {
-    return "flash_fwd gfx950: 4 waves x 32 query rows per workgroup; key tile 64 (fp32 d128: 32); "
-           "MFMA 32x32x16 bf16/f16, 32x32x2 f32; K row-major + V transposed in LDS";
+    return "flash_fwd gfx950: d128 fp16/bf16 ping-pong 8 waves x 32 query rows, 64-key tiles; "
+           "d64 fp16/bf16 4 waves x 32 rows, 2 workgroups/CU; fp32 4 waves (key tile 64, d128: 32); "
+           "MFMA 32x32x16 bf16/f16, 32x32x2 f32";
 }
 
 }  // namespace fa
