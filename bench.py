@@ -66,8 +66,11 @@ def cpu_baseline(w, q, k, v, heads: int, chunk: int, workers: int, gpu_out=None)
     import oracle
     from tiled_online_softmax_06_amd import inputs
 
-    heads = w.B * w.H if heads <= 0 else min(heads, w.B * w.H)
-    q64, k64, v64 = (inputs.to_float64(t.reshape(1, w.B * w.H, w.N, w.d)[:, :heads]) for t in (q, k, v))
+    g = w.H // k.shape[1]                     # query heads per K/V head
+    heads = w.B * w.H if heads <= 0 else max(g, min(heads, w.B * w.H) // g * g)
+    # flattened (1, B*H) query heads use flattened K/V head f // g
+    q64 = inputs.to_float64(q.reshape(1, w.B * w.H, w.N, w.d)[:, :heads])
+    k64, v64 = (inputs.to_float64(t.reshape(1, -1, w.N, w.d)[:, :heads // g]) for t in (k, v))
     scale = float(np.float32(w.scale))
     tasks = [(h, i0) for h in range(heads) for i0 in range(0, w.N, chunk)]
 
@@ -105,6 +108,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="long")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--kv-heads", type=int, default=0,
+                    help="K/V heads for a grouped-query run (0: one per query head)")
     ap.add_argument("--cpu-heads", type=int, default=0,
                     help="heads the CPU oracle computes in full (0: every head of the workload)")
     ap.add_argument("--calibrate-copy", action="store_true",
@@ -124,7 +129,11 @@ def main():
 
     w = inputs.WORKLOADS[args.workload]
     dev = torch.device("cuda:0")
-    q, k, v = inputs.make_inputs(w)
+    kv_heads = args.kv_heads or w.H
+    if w.H % kv_heads:
+        print(f"--kv-heads {kv_heads} must divide H={w.H}", file=sys.stderr)
+        sys.exit(2)
+    q, k, v = inputs.make_inputs(w, kv_heads=kv_heads)
     qd, kd, vd = (t.to(dev) for t in (q, k, v))
     o = torch.empty_like(qd)
     lse = torch.empty(qd.shape[:3], dtype=torch.float32, device=dev)
@@ -179,8 +188,8 @@ def main():
         "dtype": w.dtype,
         "data": "synthetic (seeded iid normal inputs, see tiled_online_softmax_06_amd/inputs.py)",
         "config": {"workload": f"{w.name}: B={w.B} H={w.H} N={w.N} d={w.d} {w.dtype}, non-causal, "
-                               f"scale=1/sqrt({w.d})",
-                   "B": w.B, "H": w.H, "N": w.N, "d": w.d, "causal": False},
+                               f"scale=1/sqrt({w.d})" + (f", {kv_heads} K/V heads" if kv_heads != w.H else ""),
+                   "B": w.B, "H": w.H, "N": w.N, "d": w.d, "causal": False, "kv_heads": kv_heads},
         "pct_of_mfma_peak": round(100 * tflops / peak, 2),
         "roofline": roof,
         "device": {"name": props.name, "cu": props.multi_processor_count,

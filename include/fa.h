@@ -40,7 +40,7 @@ typedef enum {
 typedef enum {
     FA_OK = 0,
     FA_ERR_NULL_POINTER = 1,          /* a tensor pointer is NULL while B*H*N > 0      */
-    FA_ERR_BAD_SHAPE = 2,             /* B, H, N or d negative, or sizes overflow       */
+    FA_ERR_BAD_SHAPE = 2,             /* a size negative, sizes overflow, H_kv !| H      */
     FA_ERR_UNSUPPORTED_HEAD_DIM = 3,  /* d is not 64 or 128                             */
     FA_ERR_UNSUPPORTED_DTYPE = 4,     /* dtype is not one of fa_dtype_t                 */
     FA_ERR_MISALIGNED = 5,            /* Q/K/V/O not 16-byte or LSE not 4-byte aligned  */
@@ -84,6 +84,26 @@ typedef enum {
 int fa_forward(const void* Q, const void* K, const void* V, void* O, float* LSE,
                int64_t B, int64_t H, int64_t N, int64_t d,
                float scale, int dtype, hipStream_t stream);
+
+/*
+ * fa_forward_gqa — the same forward pass with grouped K/V heads (grouped-query
+ * attention; H_kv = 1 is multi-query attention).  unite.ai page, section
+ * "Atención Flash-2", item 3, names both variants; this is the reading:
+ *
+ *     query head h of batch b attends to K/V head h / (H / H_kv) of batch b:
+ *       S_ij  = scale * <Q[b,h,i,:], K[b,h/g,j,:]>,   g = H / H_kv
+ *       O[b,h,i,:] = sum_j exp(S_ij) V[b,h/g,j,:] / sum_j exp(S_ij)
+ *       LSE[b,h,i] = ln sum_j exp(S_ij)
+ *
+ * Q, O     (B, H, N, d) as for fa_forward.
+ * K, V     (B, H_kv, N, d), same dtype and layout rules.
+ * H_kv     >= 1 and divides H (else FA_ERR_BAD_SHAPE, unless B*H*N == 0).
+ * Everything else (LSE, scale, dtype, stream, ownership, errors) is as for
+ * fa_forward, which is fa_forward_gqa with H_kv = H.
+ */
+int fa_forward_gqa(const void* Q, const void* K, const void* V, void* O, float* LSE,
+                   int64_t B, int64_t H, int64_t H_kv, int64_t N, int64_t d,
+                   float scale, int dtype, hipStream_t stream);
 
 /* Static, human-readable name of a return code ("unknown status" otherwise). */
 const char* fa_status_string(int status);

@@ -5,6 +5,7 @@ from .attention_ref import (  # noqa: F401
     block_state,
     empty_state,
     finalize_state,
+    kv_head,
     merge_states,
     online_blocked_ref,
 )

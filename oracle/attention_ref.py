@@ -16,7 +16,9 @@ Sources (cited by page title and section):
        Normalizzatore Online".
 
 What is computed (the plain definition, [ES] standard attention; [ES] formula
-1 and [IT] "Softmax Sicura" for the max subtraction), per head, in float64:
+1 and [IT] "Softmax Sicura" for the max subtraction), per query head, in
+float64 (with grouped K/V heads, [ES] "Atención Flash-2" item 3, the K and V of
+query head h are those of head kv_head(h)):
 
     S = scale * Q K^T          (the score matrix, materialised row chunk by chunk)
     m_i = max_j S_ij
@@ -65,24 +67,37 @@ def _head_rows(q, k, v, scale):
     return o, lse
 
 
+def kv_head(h, H, Hkv):
+    """K/V head used by query head h when H query heads share Hkv K/V heads
+    ([ES] section "Atención Flash-2", item 3: grouped-query attention; Hkv = 1
+    is multi-query attention): consecutive groups of H / Hkv query heads share
+    one K/V head."""
+    return h // (H // Hkv)
+
+
 def attention_ref(q, k, v, scale, rows=None, chunk=1024):
     """Exact attention forward in float64.
 
-    q, k, v: arrays (B, H, N, d) of any float dtype (upcast exactly to fp64).
+    q:       array (B, H, N, d) of any float dtype (upcast exactly to fp64).
+    k, v:    arrays (B, Hkv, N, d) with Hkv dividing H (Hkv = H: plain
+             attention; otherwise query head h uses K/V head kv_head(h)).
     rows:    None for every query row, or flat indices into (B, H, N).
     Returns (O, LSE): O (B, H, N, d) and LSE (B, H, N); with ``rows``,
     O (R, d) and LSE (R,) in the order of ``rows``.
     """
     q, k, v = _f64(q), _f64(k), _f64(v)
     B, H, N, d = q.shape
+    Hkv = k.shape[1]
+    assert Hkv >= 1 and H % Hkv == 0 and v.shape[1] == Hkv
     if rows is None:
         o = np.empty((B, H, N, v.shape[-1]))
         lse = np.empty((B, H, N))
         for b in range(B):
             for h in range(H):
+                g = kv_head(h, H, Hkv)
                 for i0 in range(0, N, chunk):
                     i1 = min(i0 + chunk, N)
-                    o[b, h, i0:i1], lse[b, h, i0:i1] = _head_rows(q[b, h, i0:i1], k[b, h], v[b, h], scale)
+                    o[b, h, i0:i1], lse[b, h, i0:i1] = _head_rows(q[b, h, i0:i1], k[b, g], v[b, g], scale)
         return o, lse
     rows = np.asarray(rows, dtype=np.int64)
     o = np.empty((rows.size, v.shape[-1]))
@@ -91,7 +106,8 @@ def attention_ref(q, k, v, scale, rows=None, chunk=1024):
     for hid in np.unique(heads):
         sel = np.nonzero(heads == hid)[0]
         b, h = divmod(int(hid), H)
-        o[sel], lse[sel] = _head_rows(q[b, h, rows[sel] % N], k[b, h], v[b, h], scale)
+        g = kv_head(h, H, Hkv)
+        o[sel], lse[sel] = _head_rows(q[b, h, rows[sel] % N], k[b, g], v[b, g], scale)
     return o, lse
 
 

@@ -211,6 +211,49 @@ def pin_row_subset(orc):
     _close(lse_r, lse.reshape(-1)[rows], what="rows LSE")
 
 
+def pin_grouped_heads_library(orc):
+    """Grouped K/V heads ([ES] "Atención Flash-2", item 3): agreement with
+    torch's float64 scaled_dot_product_attention with enable_gqa=True (which
+    also assigns consecutive query heads to a K/V head) for several groupings,
+    including one K/V head (multi-query)."""
+    import torch
+    from scipy.special import logsumexp
+
+    r = _rng(40)
+    for H, Hkv in ((4, 2), (6, 3), (4, 1), (3, 3)):
+        q = r.standard_normal((2, H, 11, 5))
+        k = r.standard_normal((2, Hkv, 11, 5))
+        v = r.standard_normal((2, Hkv, 11, 3))
+        s = 0.6
+        o, lse = orc.attention_ref(q, k, v, s, chunk=4)
+        ot = torch.nn.functional.scaled_dot_product_attention(
+            torch.from_numpy(q), torch.from_numpy(k), torch.from_numpy(v), scale=s, enable_gqa=True).numpy()
+        _close(o, ot, tol=1e-12, what=f"GQA O vs torch SDPA, H={H} Hkv={Hkv}")
+        g = H // Hkv
+        kk = np.stack([k[:, h // g] for h in range(H)], axis=1)
+        ref_lse = logsumexp(s * np.einsum("bhid,bhjd->bhij", q, kk), axis=-1)
+        _close(lse, ref_lse, tol=1e-12, what=f"GQA LSE, H={H} Hkv={Hkv}")
+
+
+def pin_multi_query_heads_independent(orc):
+    """One shared K/V head: each query head's output depends only on its own
+    queries, so permuting the query heads permutes O and LSE, and a head's
+    result equals the single-head problem with that head alone."""
+    r = _rng(41)
+    q = r.standard_normal((1, 5, 9, 4))
+    k = r.standard_normal((1, 1, 9, 4))
+    v = r.standard_normal((1, 1, 9, 2))
+    o, lse = orc.attention_ref(q, k, v, 0.9)
+    perm = np.array([3, 0, 4, 1, 2])
+    o_p, lse_p = orc.attention_ref(q[:, perm], k, v, 0.9)
+    _close(o_p, o[:, perm], what="MQA head permutation O")
+    _close(lse_p, lse[:, perm], what="MQA head permutation LSE")
+    for h in range(5):
+        o1, l1 = orc.attention_ref(q[:, h:h + 1], k, v, 0.9)
+        _close(o1[:, 0], o[:, h], what=f"MQA head {h} alone O")
+        _close(l1[:, 0], lse[:, h], what=f"MQA head {h} alone LSE")
+
+
 DEFINITION_PINS = [
     pin_rows_are_probabilities,
     pin_shift_invariance,
@@ -224,6 +267,8 @@ DEFINITION_PINS = [
     pin_hand_examples,
     pin_library_attention,
     pin_row_subset,
+    pin_grouped_heads_library,
+    pin_multi_query_heads_independent,
 ]
 
 

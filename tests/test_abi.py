@@ -36,7 +36,7 @@ def _header_enum(name):
 
 def test_exports_every_declared_function(lib):
     funcs = _header_functions()
-    assert set(funcs) == {"fa_forward", "fa_status_string", "fa_version"}
+    assert set(funcs) == {"fa_forward", "fa_forward_gqa", "fa_status_string", "fa_version"}
     out = subprocess.run(["nm", "-D", "--defined-only", lib._name], capture_output=True, text=True).stdout
     exported = set(re.findall(r" T (\w+)$", out, flags=re.M))
     for f in funcs:
@@ -103,3 +103,25 @@ def test_error_codes(lib):
 def test_empty_problem_is_a_no_op(lib):
     for shape in ({"B": 0}, {"H": 0}, {"N": 0}):
         assert call(lib, q=None, k=None, v=None, o=None, lse=None, **shape) == 0
+
+
+def call_gqa(lib, q=A, k=A + 64 * MB, v=A + 128 * MB, o=A + 192 * MB, lse=A + 256 * MB,
+             B=1, H=4, Hkv=2, N=128, d=64, scale=0.125, dtype=2):
+    return lib.fa_forward_gqa(q, k, v, o, lse, B, H, Hkv, N, d, scale, dtype, None)
+
+
+def test_gqa_error_codes(lib):
+    codes = _header_enum("fa_status_t")
+    lib.fa_forward_gqa.argtypes = [ctypes.c_void_p] * 5 + [ctypes.c_int64] * 5 + [
+        ctypes.c_float, ctypes.c_int, ctypes.c_void_p]
+    assert call_gqa(lib, Hkv=3) == codes["FA_ERR_BAD_SHAPE"]      # does not divide H
+    assert call_gqa(lib, Hkv=0) == codes["FA_ERR_BAD_SHAPE"]
+    assert call_gqa(lib, Hkv=-2) == codes["FA_ERR_BAD_SHAPE"]
+    assert call_gqa(lib, Hkv=8) == codes["FA_ERR_BAD_SHAPE"]      # more K/V heads than query heads
+    assert call_gqa(lib, d=80) == codes["FA_ERR_UNSUPPORTED_HEAD_DIM"]
+    assert call_gqa(lib, k=A + 64 * MB + 4) == codes["FA_ERR_MISALIGNED"]
+    # O overlapping the (smaller) K: K spans B*Hkv*N*d*2 = 32 KiB here
+    assert call_gqa(lib, o=A + 64 * MB + 32768 - 16) == codes["FA_ERR_ALIAS"]
+    assert call_gqa(lib, q=None, k=None, v=None, o=None, lse=None, N=0) == 0
+    for bad in (math.nan, math.inf):
+        assert call_gqa(lib, scale=bad) == codes["FA_ERR_BAD_SCALE"]

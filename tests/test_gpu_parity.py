@@ -189,3 +189,31 @@ def test_aliased_output_rejected_on_device():
     lse = torch.empty((1, 1, 64), dtype=torch.float32, device=DEV)
     with pytest.raises(RuntimeError, match="overlaps"):
         fa.forward_into(q, k, v, q, lse)
+
+
+@pytest.mark.parametrize("dtype", ["fp32", "fp16", "bf16"])
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("H,Hkv", [(8, 2), (6, 1), (4, 4)])
+def test_grouped_kv_heads(dtype, d, H, Hkv):
+    """Grouped-query (Hkv < H) and multi-query (Hkv = 1) attention through
+    fa_forward_gqa against the oracle, on a ragged and a tile-multiple N."""
+    for n in (200, 256):
+        q, k, v = inputs.random_qkv((2, H, n, d), dtype, seed=300 + n + d + H, kv_heads=Hkv)
+        scale = 1.0 / math.sqrt(d)
+        o, lse = run(q, k, v, scale)
+        ref_o, ref_lse = oracle_full(q, k, v, scale)
+        check(o, lse, ref_o, ref_lse, dtype, f"{dtype} d={d} H={H} Hkv={Hkv} N={n}")
+
+
+def test_grouped_kv_heads_long():
+    """Grouped-query attention at the long workload's size (B=2, H=16, 4 K/V
+    heads, N=8192, d=128, bf16) on sampled rows including tile edges."""
+    w = inputs.WORKLOADS["long"]
+    q, k, v = inputs.make_inputs(w, kv_heads=4)
+    o, lse = run(q, k, v, w.scale)
+    edges = np.array([0, 255, 256, w.N - 1])
+    heads = np.arange(w.B * w.H)[:, None] * w.N
+    rows = np.union1d(inputs.sample_rows(w, 512), (heads + edges).ravel())
+    ref_o, ref_lse = oracle.attention_ref(inputs.to_float64(q), inputs.to_float64(k), inputs.to_float64(v),
+                                          f32(w.scale), rows=rows)
+    check(o.reshape(-1, w.d)[rows], lse.reshape(-1)[rows], ref_o, ref_lse, "bf16", "long GQA 16/4")

@@ -139,8 +139,12 @@ def _finalize_lse_no_max(st):
     return st.o / st.l[:, None], np.log(st.l)
 
 
+def _kv_head_modulo(h, H, Hkv):
+    return h % Hkv
+
+
 ORIG = {n: getattr(ref, n) for n in ("attention_ref", "_head_rows", "_factor", "merge_states",
-                                     "online_blocked_ref", "finalize_state", "block_state")}
+                                     "online_blocked_ref", "finalize_state", "block_state", "kv_head")}
 
 MUTANTS = {f"rows:{k}": {"_head_rows": f} for k, f in ROW_MUTANTS.items()}
 MUTANTS.update({
@@ -153,6 +157,7 @@ MUTANTS.update({
     "online:output_not_rescaled": {"online_blocked_ref": _online_without_output_rescale},
     "online:block_off_by_one": {"online_blocked_ref": _online_block_off_by_one},
     "finalize:lse_without_max": {"finalize_state": _finalize_lse_no_max},
+    "gqa:kv_head_modulo": {"kv_head": _kv_head_modulo},
 })
 
 

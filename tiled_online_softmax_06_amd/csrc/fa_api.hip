@@ -22,22 +22,26 @@ bool mul_ok(int64_t x, int64_t y, int64_t* out) {
 
 }  // namespace
 
-extern "C" int fa_forward(const void* Q, const void* K, const void* V, void* O, float* LSE,
-                          int64_t B, int64_t H, int64_t N, int64_t d,
-                          float scale, int dtype, hipStream_t stream) {
-    if (B < 0 || H < 0 || N < 0 || d < 0) return FA_ERR_BAD_SHAPE;
+extern "C" int fa_forward_gqa(const void* Q, const void* K, const void* V, void* O, float* LSE,
+                              int64_t B, int64_t H, int64_t Hkv, int64_t N, int64_t d,
+                              float scale, int dtype, hipStream_t stream) {
+    if (B < 0 || H < 0 || N < 0 || d < 0 || Hkv < 0) return FA_ERR_BAD_SHAPE;
     if (dtype != FA_DTYPE_FP32 && dtype != FA_DTYPE_FP16 && dtype != FA_DTYPE_BF16)
         return FA_ERR_UNSUPPORTED_DTYPE;
     if (d != 64 && d != 128) return FA_ERR_UNSUPPORTED_HEAD_DIM;
     if (!isfinite(scale)) return FA_ERR_BAD_SCALE;
 
-    int64_t bh = 0, rows = 0, elems = 0, bytes = 0;
+    const int64_t esize = dtype == FA_DTYPE_FP32 ? 4 : 2;
+    int64_t bh = 0, rows = 0, elems = 0, bytes = 0, bkv = 0, kvrows = 0, kvelems = 0, kvbytes = 0;
     if (!mul_ok(B, H, &bh) || !mul_ok(bh, N, &rows) || !mul_ok(rows, d, &elems) ||
-        !mul_ok(elems, dtype == FA_DTYPE_FP32 ? 4 : 2, &bytes))
+        !mul_ok(elems, esize, &bytes) || !mul_ok(B, Hkv, &bkv) || !mul_ok(bkv, N, &kvrows) ||
+        !mul_ok(kvrows, d, &kvelems) || !mul_ok(kvelems, esize, &kvbytes))
         return FA_ERR_BAD_SHAPE;
     if (rows == 0) return FA_OK;
+    // every query head needs a K/V head: Hkv >= 1 and divides H
+    if (Hkv == 0 || H % Hkv != 0) return FA_ERR_BAD_SHAPE;
     // Kernel index limits: N and the workgroup count are 32-bit.
-    if (N > INT32_MAX) return FA_ERR_BAD_SHAPE;
+    if (N > INT32_MAX || H > INT32_MAX) return FA_ERR_BAD_SHAPE;
     const int64_t tiles = bh * ((N + fa::kMinRowsPerWorkgroup - 1) / fa::kMinRowsPerWorkgroup);
     if (tiles > INT32_MAX) return FA_ERR_BAD_SHAPE;
 
@@ -45,13 +49,19 @@ extern "C" int fa_forward(const void* Q, const void* K, const void* V, void* O, 
     if (((uintptr_t)Q | (uintptr_t)K | (uintptr_t)V | (uintptr_t)O) & 15u) return FA_ERR_MISALIGNED;
     if ((uintptr_t)LSE & 3u) return FA_ERR_MISALIGNED;
     const int64_t lbytes = rows * 4;
-    if (overlaps(O, bytes, Q, bytes) || overlaps(O, bytes, K, bytes) || overlaps(O, bytes, V, bytes) ||
-        overlaps(LSE, lbytes, Q, bytes) || overlaps(LSE, lbytes, K, bytes) ||
-        overlaps(LSE, lbytes, V, bytes) || overlaps(LSE, lbytes, O, bytes))
+    if (overlaps(O, bytes, Q, bytes) || overlaps(O, bytes, K, kvbytes) || overlaps(O, bytes, V, kvbytes) ||
+        overlaps(LSE, lbytes, Q, bytes) || overlaps(LSE, lbytes, K, kvbytes) ||
+        overlaps(LSE, lbytes, V, kvbytes) || overlaps(LSE, lbytes, O, bytes))
         return FA_ERR_ALIAS;
 
-    fa::FwdArgs a{Q, K, V, O, LSE, bh, N, (int)d, dtype, scale};
+    fa::FwdArgs a{Q, K, V, O, LSE, bh, H, Hkv, N, (int)d, dtype, scale};
     return fa::launch_forward(a, stream) == hipSuccess ? FA_OK : FA_ERR_LAUNCH;
+}
+
+extern "C" int fa_forward(const void* Q, const void* K, const void* V, void* O, float* LSE,
+                          int64_t B, int64_t H, int64_t N, int64_t d,
+                          float scale, int dtype, hipStream_t stream) {
+    return fa_forward_gqa(Q, K, V, O, LSE, B, H, H, N, d, scale, dtype, stream);
 }
 
 extern "C" const char* fa_status_string(int status) {

@@ -13,7 +13,9 @@ struct FwdArgs {
     const void* v;
     void* o;
     float* lse;
-    int64_t bh;      // B * H (heads are independent and contiguous)
+    int64_t bh;      // B * H (query heads are independent and contiguous)
+    int64_t h;       // H, query heads per batch
+    int64_t hkv;     // K/V heads per batch (divides H)
     int64_t n;       // sequence length
     int d;           // head dimension (64 or 128)
     int dtype;       // fa_dtype_t

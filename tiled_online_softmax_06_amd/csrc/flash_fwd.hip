@@ -175,7 +175,7 @@ template <typename T, int D, int BC, int NW>
 __global__ void __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2)))
 flash_fwd_16(const T* __restrict__ Q, const T* __restrict__ K, const T* __restrict__ V,
              T* __restrict__ O, float* __restrict__ LSE,
-             int n, int qtiles, int total, float c, int negate)
+             int n, int qtiles, int total, float c, int negate, int nh, int grp)
 {
     using M = Mfma<T>;
     constexpr int BR = 32 * NW;
@@ -206,6 +206,9 @@ flash_fwd_16(const T* __restrict__ Q, const T* __restrict__ K, const T* __restri
     const int bh = tile / qtiles;
     const int qt = tile - bh * qtiles;
     const int64_t base = (int64_t)bh * n * D;
+    // K/V head of this query head: query heads h of a batch share K/V head
+    // h / grp (grp = 1: one K/V head per query head).
+    const int64_t kvbase = (int64_t)((bh / nh) * (nh / grp) + (bh % nh) / grp) * n * D;
     const int qrow = qt * BR + wave * 32 + col;
 
     // Q^T as the B operand: lane (col, half) holds Q[qrow][16*kc + 8*half + 0..7]
@@ -223,9 +226,9 @@ flash_fwd_16(const T* __restrict__ Q, const T* __restrict__ K, const T* __restri
     // Per-head buffer resources: any offset past the head reads zero instead
     // of faulting (the tail below also clamps, so this is a safety net).
     const __amdgpu_buffer_rsrc_t krs =
-        __builtin_amdgcn_make_buffer_rsrc((void*)(K + base), (short)0, n * ROWB, 0x00020000);
+        __builtin_amdgcn_make_buffer_rsrc((void*)(K + kvbase), (short)0, n * ROWB, 0x00020000);
     const __amdgpu_buffer_rsrc_t vrs =
-        __builtin_amdgcn_make_buffer_rsrc((void*)(V + base), (short)0, n * ROWB, 0x00020000);
+        __builtin_amdgcn_make_buffer_rsrc((void*)(V + kvbase), (short)0, n * ROWB, 0x00020000);
 
     // DMA source offsets of this lane for the wave's units (within a tile).
     const int lrow = lane / CPR;             // row inside a unit
@@ -419,7 +422,7 @@ template <typename T, int D>
 __global__ void __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2)))
 flash_fwd_pp(const T* __restrict__ Q, const T* __restrict__ K, const T* __restrict__ V,
              T* __restrict__ O, float* __restrict__ LSE,
-             int n, int qtiles, int total, float c, int negate)
+             int n, int qtiles, int total, float c, int negate, int nh, int grp)
 {
     using M = Mfma<T>;
     constexpr int NW = 8;
@@ -454,6 +457,9 @@ flash_fwd_pp(const T* __restrict__ Q, const T* __restrict__ K, const T* __restri
     const int bh = tile / qtiles;
     const int qt = tile - bh * qtiles;
     const int64_t base = (int64_t)bh * n * D;
+    // K/V head of this query head: query heads h of a batch share K/V head
+    // h / grp (grp = 1: one K/V head per query head).
+    const int64_t kvbase = (int64_t)((bh / nh) * (nh / grp) + (bh % nh) / grp) * n * D;
     const int qrow = qt * BR + wave * 32 + col;
 
     // Q^T as the B operand: lane (col, half) holds Q[qrow][16 kc + 8 half + 0..7];
@@ -469,9 +475,9 @@ flash_fwd_pp(const T* __restrict__ Q, const T* __restrict__ K, const T* __restri
     }
 
     const __amdgpu_buffer_rsrc_t krs =
-        __builtin_amdgcn_make_buffer_rsrc((void*)(K + base), (short)0, n * ROWB, 0x00020000);
+        __builtin_amdgcn_make_buffer_rsrc((void*)(K + kvbase), (short)0, n * ROWB, 0x00020000);
     const __amdgpu_buffer_rsrc_t vrs =
-        __builtin_amdgcn_make_buffer_rsrc((void*)(V + base), (short)0, n * ROWB, 0x00020000);
+        __builtin_amdgcn_make_buffer_rsrc((void*)(V + kvbase), (short)0, n * ROWB, 0x00020000);
 
     // DMA: this wave moves units gw*UPW .. of a tile; K and V use their own
     // swizzles (chosen by the global chunk each lane fetches).
@@ -716,7 +722,7 @@ template <int D, int BC, int NW>
 __global__ void __launch_bounds__(NW * 64)
 flash_fwd_32(const float* __restrict__ Q, const float* __restrict__ K, const float* __restrict__ V,
              float* __restrict__ O, float* __restrict__ LSE,
-             int n, int qtiles, int total, float c, int negate)
+             int n, int qtiles, int total, float c, int negate, int nh, int grp)
 {
     constexpr int NT = NW * 64;
     constexpr int BR = 32 * NW;
@@ -739,9 +745,12 @@ flash_fwd_32(const float* __restrict__ Q, const float* __restrict__ K, const flo
     const int bh = tile / qtiles;
     const int qt = tile - bh * qtiles;
     const int64_t base = (int64_t)bh * n * D;
+    // K/V head of this query head: query heads h of a batch share K/V head
+    // h / grp (grp = 1: one K/V head per query head).
+    const int64_t kvbase = (int64_t)((bh / nh) * (nh / grp) + (bh % nh) / grp) * n * D;
     const float* __restrict__ Qh = Q + base;
-    const float* __restrict__ Kh = K + base;
-    const float* __restrict__ Vh = V + base;
+    const float* __restrict__ Kh = K + kvbase;
+    const float* __restrict__ Vh = V + kvbase;
     const int qrow = qt * BR + wave * 32 + col;
 
     // Q^T as the B operand: lane (col, half) holds Q[qrow][2*kc + half].
@@ -886,7 +895,9 @@ hipError_t launch(Kern kern, int nw, int br, const FwdArgs& a, hipStream_t strea
     const T* v = (const T*)a.v;
     T* o = (T*)a.o;
     float* lse = a.lse;
-    void* args[] = {&q, &k, &v, &o, &lse, (void*)&n, (void*)&qtiles, (void*)&total, (void*)&c, (void*)&negate};
+    const int nh = (int)a.h, grp = (int)(a.h / a.hkv);
+    void* args[] = {&q, &k, &v, &o, &lse, (void*)&n, (void*)&qtiles, (void*)&total, (void*)&c, (void*)&negate,
+                    (void*)&nh, (void*)&grp};
     return hipLaunchKernel((const void*)kern, dim3(total), dim3(nw * 64), args, 0, stream);
 }
 

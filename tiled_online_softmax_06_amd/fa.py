@@ -33,6 +33,9 @@ def load_library():
         lib.fa_forward.argtypes = [ctypes.c_void_p] * 5 + [ctypes.c_int64] * 4 + [
             ctypes.c_float, ctypes.c_int, ctypes.c_void_p]
         lib.fa_forward.restype = ctypes.c_int
+        lib.fa_forward_gqa.argtypes = [ctypes.c_void_p] * 5 + [ctypes.c_int64] * 5 + [
+            ctypes.c_float, ctypes.c_int, ctypes.c_void_p]
+        lib.fa_forward_gqa.restype = ctypes.c_int
         lib.fa_status_string.argtypes = [ctypes.c_int]
         lib.fa_status_string.restype = ctypes.c_char_p
         lib.fa_version.argtypes = []
@@ -46,7 +49,10 @@ def status_string(code: int) -> str:
 
 
 def forward_into(q, k, v, o, lse, scale: float | None = None, stream=None) -> None:
-    """O and LSE are written in place; all five tensors are on one GPU."""
+    """O and LSE are written in place; all five tensors are on one GPU.
+
+    q, o: (B, H, N, d); k, v: (B, H_kv, N, d) with H_kv dividing H (H_kv < H:
+    grouped-query attention through fa_forward_gqa; H_kv = H: fa_forward)."""
     lib = load_library()
     for name, t in (("q", q), ("k", k), ("v", v), ("o", o), ("lse", lse)):
         if not t.is_cuda:
@@ -57,8 +63,10 @@ def forward_into(q, k, v, o, lse, scale: float | None = None, stream=None) -> No
         raise ValueError(f"q, k, v, o must share one of {list(FA_DTYPE)}")
     if lse.dtype != torch.float32:
         raise ValueError("lse must be float32")
-    if q.dim() != 4 or k.shape != q.shape or v.shape != q.shape or o.shape != q.shape:
-        raise ValueError("q, k, v, o must all have shape (B, H, N, d)")
+    if q.dim() != 4 or o.shape != q.shape or k.dim() != 4 or v.shape != k.shape:
+        raise ValueError("q, o must have shape (B, H, N, d) and k, v one shape (B, H_kv, N, d)")
+    if k.shape[0] != q.shape[0] or k.shape[2:] != q.shape[2:] or k.shape[1] < 1 or q.shape[1] % k.shape[1]:
+        raise ValueError("k, v must be (B, H_kv, N, d) with H_kv dividing H")
     if tuple(lse.shape) != tuple(q.shape[:3]):
         raise ValueError("lse must have shape (B, H, N)")
     B, H, N, d = q.shape
@@ -68,8 +76,12 @@ def forward_into(q, k, v, o, lse, scale: float | None = None, stream=None) -> No
         stream = torch.cuda.current_stream(q.device)
     handle = stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
     with torch.cuda.device(q.device):
-        rc = lib.fa_forward(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(),
-                            B, H, N, d, float(scale), FA_DTYPE[q.dtype], handle)
+        if k.shape[1] == H:
+            rc = lib.fa_forward(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(),
+                                B, H, N, d, float(scale), FA_DTYPE[q.dtype], handle)
+        else:
+            rc = lib.fa_forward_gqa(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(),
+                                    B, H, k.shape[1], N, d, float(scale), FA_DTYPE[q.dtype], handle)
     if rc != 0:
         raise RuntimeError(f"fa_forward failed: {status_string(rc)} ({rc})")
 

@@ -81,30 +81,36 @@ WORKLOADS = {
 }
 
 
-def make_inputs(w: Workload, seed: int | None = None):
-    """Return (q, k, v) as contiguous CPU tensors in the workload's dtype."""
+def make_inputs(w: Workload, seed: int | None = None, kv_heads: int | None = None):
+    """Return (q, k, v) as contiguous CPU tensors in the workload's dtype.
+
+    kv_heads (default H): number of K/V heads for grouped-query runs; K and V
+    then have shape (B, kv_heads, N, d) and are drawn after Q as usual."""
     rng = np.random.default_rng(w.seed if seed is None else seed)
     shape = (w.B, w.H, w.N, w.d)
+    kv_shape = (w.B, w.H if kv_heads is None else kv_heads, w.N, w.d)
     q = rng.standard_normal(shape, dtype=np.float32)
     if w.qk_sigma != 1.0:
         q *= np.float32(w.qk_sigma)
-    k = rng.standard_normal(shape, dtype=np.float32)
+    k = rng.standard_normal(kv_shape, dtype=np.float32)
     if w.qk_sigma != 1.0:
         k *= np.float32(w.qk_sigma)
     if w.v_dist == "uniform":
-        v = rng.uniform(-1.0, 1.0, size=shape).astype(np.float32)
+        v = rng.uniform(-1.0, 1.0, size=kv_shape).astype(np.float32)
     else:
-        v = rng.standard_normal(shape, dtype=np.float32)
+        v = rng.standard_normal(kv_shape, dtype=np.float32)
     dt = DTYPES[w.dtype]
     return tuple(torch.from_numpy(x).to(dt).contiguous() for x in (q, k, v))
 
 
-def random_qkv(shape, dtype: str, seed: int, sigma: float = 1.0):
-    """Generic seeded (q, k, v) of any shape (B, H, N, d), N(0, sigma) each."""
+def random_qkv(shape, dtype: str, seed: int, sigma: float = 1.0, kv_heads: int | None = None):
+    """Generic seeded (q, k, v): q of shape (B, H, N, d), k and v of shape
+    (B, kv_heads or H, N, d); N(0, sigma) each."""
     rng = np.random.default_rng(seed)
     out = []
-    for _ in range(3):
-        x = rng.standard_normal(shape, dtype=np.float32)
+    kv_shape = tuple(shape) if kv_heads is None else (shape[0], kv_heads) + tuple(shape[2:])
+    for i in range(3):
+        x = rng.standard_normal(shape if i == 0 else kv_shape, dtype=np.float32)
         if sigma != 1.0:
             x *= np.float32(sigma)
         out.append(torch.from_numpy(x).to(DTYPES[dtype]).contiguous())
