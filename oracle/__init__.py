@@ -1,6 +1,7 @@
 """CPU oracle (test infrastructure only; see attention_ref)."""
 from .attention_ref import (  # noqa: F401
     State,
+    attention_bwd_ref,
     attention_ref,
     block_state,
     empty_state,

@@ -172,3 +172,45 @@ def online_blocked_ref(q, k, v, scale, bounds):
         st = State(m_new, alpha * st.l + p.sum(axis=1), alpha[:, None] * st.o + p @ v[j0:j1])
         j0 = j1
     return finalize_state(st)
+
+
+def attention_bwd_ref(q, k, v, do, scale):
+    """Gradients of the attention forward in float64: (dQ, dK, dV).
+
+    Backward of the definition above, with S and P recomputed from Q and K
+    rather than stored ([ES] "Introducción a la Atención Flash", item 2, and
+    [IT], the recomputation idea; [ES] "Atención Flash-2", item 2, the
+    backward pass).  Per query head, with D_i = sum_e dO_ie O_ie:
+
+        S = scale Q K^T,  P = softmax(S) (rows),  O = P V
+        dV = P^T dO
+        dP = dO V^T
+        dS = P * (dP - D)          (elementwise, D broadcast along rows)
+        dQ = scale dS K
+        dK = scale dS^T Q
+
+    q, do: (B, H, N, d); k, v: (B, Hkv, N, d) with Hkv dividing H.  With
+    grouped K/V heads the gradients of a K/V head add up over the query heads
+    that use it.  Returns dQ (B, H, N, d), dK and dV (B, Hkv, N, d).
+    """
+    q, k, v, do = _f64(q), _f64(k), _f64(v), _f64(do)
+    B, H, N, d = q.shape
+    Hkv = k.shape[1]
+    assert Hkv >= 1 and H % Hkv == 0 and v.shape[1] == Hkv
+    dq = np.zeros_like(q)
+    dk = np.zeros_like(k)
+    dv = np.zeros_like(v)
+    for b in range(B):
+        for h in range(H):
+            g = kv_head(h, H, Hkv)
+            s = scale * (q[b, h] @ k[b, g].T)
+            p = np.exp(s - s.max(axis=1, keepdims=True))
+            p /= p.sum(axis=1, keepdims=True)
+            o = p @ v[b, g]
+            dv[b, g] += p.T @ do[b, h]
+            dp = do[b, h] @ v[b, g].T
+            dd = np.sum(do[b, h] * o, axis=1, keepdims=True)
+            ds = p * (dp - dd)
+            dq[b, h] = scale * (ds @ k[b, g])
+            dk[b, g] += scale * (ds.T @ q[b, h])
+    return dq, dk, dv

@@ -354,10 +354,85 @@ def pin_merge_with_sharp_maxima(orc):
     _close(lse, [700.0], what="empty-state identity LSE")
 
 
+# ---------------------------------------------------------------------------
+# The backward pass (gradients of the definition, S and P recomputed)
+# ---------------------------------------------------------------------------
+
+def _bwd_case(seed, B=1, H=2, Hkv=2, N=7, d=4, dv=3):
+    r = _rng(seed)
+    return (r.standard_normal((B, H, N, d)), r.standard_normal((B, Hkv, N, d)),
+            r.standard_normal((B, Hkv, N, dv)), r.standard_normal((B, H, N, dv)))
+
+
+def pin_bwd_autograd(orc):
+    """Gradients agree with torch autograd (float64) through torch's
+    scaled_dot_product_attention, including grouped K/V heads."""
+    import torch
+
+    for seed, H, Hkv in ((50, 2, 2), (51, 4, 2), (52, 3, 1)):
+        q, k, v, do = _bwd_case(seed, B=2, H=H, Hkv=Hkv, N=9)
+        dq, dk, dv = orc.attention_bwd_ref(q, k, v, do, 0.45)
+        qt, kt, vt = (torch.tensor(x, requires_grad=True) for x in (q, k, v))
+        o = torch.nn.functional.scaled_dot_product_attention(qt, kt, vt, scale=0.45, enable_gqa=True)
+        o.backward(torch.tensor(do))
+        _close(dq, qt.grad.numpy(), what=f"dQ vs autograd H={H} Hkv={Hkv}")
+        _close(dk, kt.grad.numpy(), what=f"dK vs autograd H={H} Hkv={Hkv}")
+        _close(dv, vt.grad.numpy(), what=f"dV vs autograd H={H} Hkv={Hkv}")
+
+
+def pin_bwd_finite_differences(orc):
+    """Directional derivatives of f = <dO, O(Q, K, V)> by central differences
+    of the forward oracle match <grad, direction> for each input."""
+    q, k, v, do = _bwd_case(53, H=2, Hkv=1, N=6, d=3, dv=2)
+    s = 0.8
+    dq, dk, dv = orc.attention_bwd_ref(q, k, v, do, s)
+    r = _rng(54)
+    eps = 1e-5
+
+    def f(q_, k_, v_):
+        return float(np.sum(do * orc.attention_ref(q_, k_, v_, s)[0]))
+
+    for name, grad in (("Q", dq), ("K", dk), ("V", dv)):
+        dirn = r.standard_normal(grad.shape)
+        args_p = [q, k, v]
+        args_m = [q, k, v]
+        i = "QKV".index(name)
+        args_p[i] = args_p[i] + eps * dirn
+        args_m[i] = args_m[i] - eps * dirn
+        fd = (f(*args_p) - f(*args_m)) / (2 * eps)
+        an = float(np.sum(grad * dirn))
+        assert abs(fd - an) <= 1e-7 * max(1.0, abs(an)), f"d{name}: finite difference {fd} vs {an}"
+
+
+def pin_bwd_sums(orc):
+    """Rows of P sum to one and rows of dS sum to zero, so per head the key
+    gradients sum to zero (sum_j dK_j = 0) and the value gradients sum to the
+    upstream gradients (sum_j dV_j = sum_i dO_i); the gradient is linear in dO
+    and vanishes with it."""
+    q, k, v, do = _bwd_case(55, B=2, H=3, Hkv=3, N=8)
+    dq, dk, dv = orc.attention_bwd_ref(q, k, v, do, 1.1)
+    _close(dk.sum(axis=2), np.zeros((2, 3, 4)), tol=1e-12, what="sum of dK over keys")
+    _close(dv.sum(axis=2), do.sum(axis=2), tol=1e-12, what="sum of dV over keys")
+    dq2, dk2, dv2 = orc.attention_bwd_ref(q, k, v, 2.5 * do, 1.1)
+    _close(dq2, 2.5 * dq, what="dQ linear in dO")
+    _close(dk2, 2.5 * dk, what="dK linear in dO")
+    _close(dv2, 2.5 * dv, what="dV linear in dO")
+    z = orc.attention_bwd_ref(q, k, v, np.zeros_like(do), 1.1)
+    for name, g in zip("QKV", z):
+        _close(g, np.zeros_like(g), what=f"d{name} with zero upstream gradient")
+
+
+BACKWARD_PINS = [
+    pin_bwd_autograd,
+    pin_bwd_finite_differences,
+    pin_bwd_sums,
+]
+
+
 BLOCKED_PINS = [
     pin_every_contiguous_partition,
     pin_random_merge_trees,
     pin_merge_with_sharp_maxima,
 ]
 
-ALL_PINS = DEFINITION_PINS + BLOCKED_PINS
+ALL_PINS = DEFINITION_PINS + BLOCKED_PINS + BACKWARD_PINS

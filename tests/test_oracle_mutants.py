@@ -143,8 +143,38 @@ def _kv_head_modulo(h, H, Hkv):
     return h % Hkv
 
 
+def _bwd_variant(no_d=False, dq_no_scale=False, dk_from_p=False, overwrite=False, dv_from_ds=False):
+    """attention_bwd_ref with one planted slip."""
+    def bwd(q, k, v, do, scale):
+        q, k, v, do = (np.asarray(x, dtype=np.float64) for x in (q, k, v, do))
+        B, H, N, d = q.shape
+        Hkv = k.shape[1]
+        dq, dk, dv = np.zeros_like(q), np.zeros_like(k), np.zeros_like(v)
+        for b in range(B):
+            for h in range(H):
+                g = h // (H // Hkv)
+                s = scale * (q[b, h] @ k[b, g].T)
+                p = np.exp(s - s.max(axis=1, keepdims=True))
+                p /= p.sum(axis=1, keepdims=True)
+                o = p @ v[b, g]
+                dp = do[b, h] @ v[b, g].T
+                dd = 0.0 if no_d else np.sum(do[b, h] * o, axis=1, keepdims=True)
+                ds = p * (dp - dd)
+                gv = (ds if dv_from_ds else p).T @ do[b, h]
+                gk = (1.0 * scale) * ((p if dk_from_p else ds).T @ q[b, h])
+                if overwrite:
+                    dv[b, g], dk[b, g] = gv, gk
+                else:
+                    dv[b, g] += gv
+                    dk[b, g] += gk
+                dq[b, h] = (1.0 if dq_no_scale else scale) * (ds @ k[b, g])
+        return dq, dk, dv
+    return bwd
+
+
 ORIG = {n: getattr(ref, n) for n in ("attention_ref", "_head_rows", "_factor", "merge_states",
-                                     "online_blocked_ref", "finalize_state", "block_state", "kv_head")}
+                                     "online_blocked_ref", "finalize_state", "block_state", "kv_head",
+                                     "attention_bwd_ref")}
 
 MUTANTS = {f"rows:{k}": {"_head_rows": f} for k, f in ROW_MUTANTS.items()}
 MUTANTS.update({
@@ -158,13 +188,18 @@ MUTANTS.update({
     "online:block_off_by_one": {"online_blocked_ref": _online_block_off_by_one},
     "finalize:lse_without_max": {"finalize_state": _finalize_lse_no_max},
     "gqa:kv_head_modulo": {"kv_head": _kv_head_modulo},
+    "bwd:no_rowsum_term": {"attention_bwd_ref": _bwd_variant(no_d=True)},
+    "bwd:dq_without_scale": {"attention_bwd_ref": _bwd_variant(dq_no_scale=True)},
+    "bwd:dk_from_p": {"attention_bwd_ref": _bwd_variant(dk_from_p=True)},
+    "bwd:dv_from_ds": {"attention_bwd_ref": _bwd_variant(dv_from_ds=True)},
+    "bwd:group_grads_overwritten": {"attention_bwd_ref": _bwd_variant(overwrite=True)},
 })
 
 
 def _module_view():
     return types.SimpleNamespace(**{n: getattr(ref, n) for n in
                                     ("attention_ref", "block_state", "empty_state", "merge_states",
-                                     "finalize_state", "online_blocked_ref", "State")})
+                                     "finalize_state", "online_blocked_ref", "State", "attention_bwd_ref")})
 
 
 @pytest.mark.parametrize("name", sorted(MUTANTS))
