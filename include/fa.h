@@ -105,6 +105,45 @@ int fa_forward_gqa(const void* Q, const void* K, const void* V, void* O, float* 
                    int64_t B, int64_t H, int64_t H_kv, int64_t N, int64_t d,
                    float scale, int dtype, hipStream_t stream);
 
+/*
+ * fa_backward — gradients of fa_forward_gqa with respect to Q, K and V.
+ *
+ * The unite.ai page names recomputation in the backward pass (section
+ * "Introducción a la Atención Flash", item 2) and a faster backward pass
+ * (section "Atención Flash-2", item 2); the nisoo.com page (part 3) explains
+ * the recomputation.  This is the gradient of the forward definition, per
+ * query head h (K/V head g = h / (H / H_kv)), with P recomputed from Q, K
+ * and the forward's LSE instead of being stored:
+ *
+ *     P_ij  = exp(scale <Q_i, K_j> - LSE_i)
+ *     D_i   = sum_e dO_ie O_ie
+ *     dV_g += P^T dO
+ *     dS_ij = P_ij (sum_e dO_ie V_je - D_i)
+ *     dQ    = scale dS K,    dK_g += scale dS^T Q
+ *
+ * Q, O, dO  device, read only, (B, H, N, d) of `dtype`.
+ * K, V      device, read only, (B, H_kv, N, d).
+ * LSE       device, read only, (B, H, N) float32: the LSE that fa_forward /
+ *           fa_forward_gqa wrote for these Q, K, V and scale.
+ * Dws       device, written, (B, H, N) float32 workspace: receives D_i (the
+ *           caller allocates it; its contents on return are D).
+ * dQ        device, written, (B, H, N, d) of `dtype`.
+ * dK, dV    device, written, (B, H_kv, N, d) of `dtype`.
+ * dtype     FA_DTYPE_FP16 or FA_DTYPE_BF16 (fp32 inputs: FA_ERR_UNSUPPORTED_DTYPE).
+ *           Products run on MFMA with float32 accumulation; P and dS are
+ *           rounded to `dtype` before their second products; outputs are
+ *           rounded to `dtype`.
+ * d, scale, stream, H_kv: as for fa_forward_gqa.
+ *
+ * Ownership and errors as for fa_forward; the outputs and Dws must not
+ * overlap each other or any input (FA_ERR_ALIAS).  The call launches three
+ * kernels in stream order and returns after queueing them.
+ */
+int fa_backward(const void* Q, const void* K, const void* V, const void* O, const void* dO,
+                const float* LSE, float* Dws, void* dQ, void* dK, void* dV,
+                int64_t B, int64_t H, int64_t H_kv, int64_t N, int64_t d,
+                float scale, int dtype, hipStream_t stream);
+
 /* Static, human-readable name of a return code ("unknown status" otherwise). */
 const char* fa_status_string(int status);
 

@@ -36,7 +36,8 @@ def _header_enum(name):
 
 def test_exports_every_declared_function(lib):
     funcs = _header_functions()
-    assert set(funcs) == {"fa_forward", "fa_forward_gqa", "fa_status_string", "fa_version"}
+    assert set(funcs) == {"fa_forward", "fa_forward_gqa", "fa_backward", "fa_status_string",
+                          "fa_version"}
     out = subprocess.run(["nm", "-D", "--defined-only", lib._name], capture_output=True, text=True).stdout
     exported = set(re.findall(r" T (\w+)$", out, flags=re.M))
     for f in funcs:
@@ -82,6 +83,8 @@ def test_error_codes(lib):
     assert call(lib, d=-64) == codes["FA_ERR_BAD_SHAPE"]
     assert call(lib, B=1 << 40, H=1 << 40) == codes["FA_ERR_BAD_SHAPE"]       # size overflow
     assert call(lib, N=1 << 31) == codes["FA_ERR_BAD_SHAPE"]                  # 32-bit kernel index
+    assert call(lib, N=1 << 24, d=128) == codes["FA_ERR_BAD_SHAPE"]           # 4 GiB per head > 32-bit offsets
+    assert call(lib, N=1 << 23, d=64, dtype=0) == codes["FA_ERR_BAD_SHAPE"]
     assert call(lib, d=96) == codes["FA_ERR_UNSUPPORTED_HEAD_DIM"]
     assert call(lib, d=256) == codes["FA_ERR_UNSUPPORTED_HEAD_DIM"]
     assert call(lib, dtype=3) == codes["FA_ERR_UNSUPPORTED_DTYPE"]
@@ -125,3 +128,37 @@ def test_gqa_error_codes(lib):
     assert call_gqa(lib, q=None, k=None, v=None, o=None, lse=None, N=0) == 0
     for bad in (math.nan, math.inf):
         assert call_gqa(lib, scale=bad) == codes["FA_ERR_BAD_SCALE"]
+
+
+def call_bwd(lib, q=A, k=A + 64 * MB, v=A + 128 * MB, o=A + 192 * MB, do=A + 256 * MB, lse=A + 320 * MB,
+             dws=A + 384 * MB, dq=A + 448 * MB, dk=A + 512 * MB, dv=A + 576 * MB,
+             B=1, H=4, Hkv=2, N=128, d=64, scale=0.125, dtype=2):
+    lib.fa_backward.argtypes = [ctypes.c_void_p] * 10 + [ctypes.c_int64] * 5 + [
+        ctypes.c_float, ctypes.c_int, ctypes.c_void_p]
+    return lib.fa_backward(q, k, v, o, do, lse, dws, dq, dk, dv, B, H, Hkv, N, d, scale, dtype, None)
+
+
+def test_backward_error_codes(lib):
+    codes = _header_enum("fa_status_t")
+    assert call_bwd(lib, B=-1) == codes["FA_ERR_BAD_SHAPE"]
+    assert call_bwd(lib, Hkv=3) == codes["FA_ERR_BAD_SHAPE"]
+    assert call_bwd(lib, Hkv=0) == codes["FA_ERR_BAD_SHAPE"]
+    assert call_bwd(lib, B=1 << 40, H=1 << 40) == codes["FA_ERR_BAD_SHAPE"]
+    assert call_bwd(lib, N=1 << 24, d=64) == codes["FA_ERR_BAD_SHAPE"]       # 2 GiB per head
+    assert call_bwd(lib, dtype=0) == codes["FA_ERR_UNSUPPORTED_DTYPE"]        # fp32: forward only
+    assert call_bwd(lib, d=96) == codes["FA_ERR_UNSUPPORTED_HEAD_DIM"]
+    for bad in (math.nan, -math.inf):
+        assert call_bwd(lib, scale=bad) == codes["FA_ERR_BAD_SCALE"]
+    for field in ("q", "k", "v", "o", "do", "lse", "dws", "dq", "dk", "dv"):
+        assert call_bwd(lib, **{field: None}) == codes["FA_ERR_NULL_POINTER"], field
+    for field in ("q", "k", "v", "o", "do", "dq", "dk", "dv"):
+        assert call_bwd(lib, **{field: A + 1024 * MB + 8}) == codes["FA_ERR_MISALIGNED"], field
+    assert call_bwd(lib, dws=A + 384 * MB + 2) == codes["FA_ERR_MISALIGNED"]
+    # outputs overlapping an input or each other (Q spans 64 KiB, K 32 KiB, LSE 2 KiB)
+    assert call_bwd(lib, dq=A + 64) == codes["FA_ERR_ALIAS"]                   # dQ inside Q
+    assert call_bwd(lib, dk=A + 256 * MB + 16) == codes["FA_ERR_ALIAS"]        # dK inside dO
+    assert call_bwd(lib, dv=A + 512 * MB + 32768 - 16) == codes["FA_ERR_ALIAS"]  # dV tail of dK
+    assert call_bwd(lib, dws=A + 320 * MB + 4) == codes["FA_ERR_ALIAS"]        # workspace inside LSE
+    assert call_bwd(lib, dws=A + 448 * MB) == codes["FA_ERR_ALIAS"]            # workspace == dQ
+    assert call_bwd(lib, q=None, k=None, v=None, o=None, do=None, lse=None, dws=None, dq=None,
+                    dk=None, dv=None, N=0) == 0

@@ -40,8 +40,9 @@ extern "C" int fa_forward_gqa(const void* Q, const void* K, const void* V, void*
     if (rows == 0) return FA_OK;
     // every query head needs a K/V head: Hkv >= 1 and divides H
     if (Hkv == 0 || H % Hkv != 0) return FA_ERR_BAD_SHAPE;
-    // Kernel index limits: N and the workgroup count are 32-bit.
-    if (N > INT32_MAX || H > INT32_MAX) return FA_ERR_BAD_SHAPE;
+    // Kernel index limits: N and the workgroup count are 32-bit, and one
+    // head's K / V rows are addressed with 32-bit buffer byte offsets.
+    if (N > INT32_MAX || H > INT32_MAX || N * d * esize > INT32_MAX) return FA_ERR_BAD_SHAPE;
     const int64_t tiles = bh * ((N + fa::kMinRowsPerWorkgroup - 1) / fa::kMinRowsPerWorkgroup);
     if (tiles > INT32_MAX) return FA_ERR_BAD_SHAPE;
 
@@ -62,6 +63,48 @@ extern "C" int fa_forward(const void* Q, const void* K, const void* V, void* O, 
                           int64_t B, int64_t H, int64_t N, int64_t d,
                           float scale, int dtype, hipStream_t stream) {
     return fa_forward_gqa(Q, K, V, O, LSE, B, H, H, N, d, scale, dtype, stream);
+}
+
+extern "C" int fa_backward(const void* Q, const void* K, const void* V, const void* O, const void* dO,
+                           const float* LSE, float* Dws, void* dQ, void* dK, void* dV,
+                           int64_t B, int64_t H, int64_t Hkv, int64_t N, int64_t d,
+                           float scale, int dtype, hipStream_t stream) {
+    if (B < 0 || H < 0 || N < 0 || d < 0 || Hkv < 0) return FA_ERR_BAD_SHAPE;
+    if (dtype != FA_DTYPE_FP16 && dtype != FA_DTYPE_BF16) return FA_ERR_UNSUPPORTED_DTYPE;
+    if (d != 64 && d != 128) return FA_ERR_UNSUPPORTED_HEAD_DIM;
+    if (!isfinite(scale)) return FA_ERR_BAD_SCALE;
+
+    const int64_t esize = 2;
+    int64_t bh = 0, rows = 0, elems = 0, bytes = 0, bkv = 0, kvrows = 0, kvelems = 0, kvbytes = 0;
+    if (!mul_ok(B, H, &bh) || !mul_ok(bh, N, &rows) || !mul_ok(rows, d, &elems) ||
+        !mul_ok(elems, esize, &bytes) || !mul_ok(B, Hkv, &bkv) || !mul_ok(bkv, N, &kvrows) ||
+        !mul_ok(kvrows, d, &kvelems) || !mul_ok(kvelems, esize, &kvbytes))
+        return FA_ERR_BAD_SHAPE;
+    if (rows == 0) return FA_OK;
+    if (Hkv == 0 || H % Hkv != 0) return FA_ERR_BAD_SHAPE;
+    if (N > INT32_MAX || H > INT32_MAX || N * d * esize > INT32_MAX) return FA_ERR_BAD_SHAPE;
+    const int64_t tiles = bh * ((N + fa::kMinRowsPerWorkgroup - 1) / fa::kMinRowsPerWorkgroup);
+    if (tiles > INT32_MAX) return FA_ERR_BAD_SHAPE;
+
+    if (!Q || !K || !V || !O || !dO || !LSE || !Dws || !dQ || !dK || !dV) return FA_ERR_NULL_POINTER;
+    if (((uintptr_t)Q | (uintptr_t)K | (uintptr_t)V | (uintptr_t)O | (uintptr_t)dO | (uintptr_t)dQ |
+         (uintptr_t)dK | (uintptr_t)dV) & 15u)
+        return FA_ERR_MISALIGNED;
+    if (((uintptr_t)LSE | (uintptr_t)Dws) & 3u) return FA_ERR_MISALIGNED;
+    const int64_t lbytes = rows * 4;
+    // outputs (dQ, dK, dV, Dws) must not overlap each other or any input
+    struct Span { const void* p; int64_t n; };
+    const Span ins[] = {{Q, bytes}, {K, kvbytes}, {V, kvbytes}, {O, bytes}, {dO, bytes}, {LSE, lbytes}};
+    const Span outs[] = {{dQ, bytes}, {dK, kvbytes}, {dV, kvbytes}, {Dws, lbytes}};
+    for (int i = 0; i < 4; ++i) {
+        for (const Span& in : ins)
+            if (overlaps(outs[i].p, outs[i].n, in.p, in.n)) return FA_ERR_ALIAS;
+        for (int j = i + 1; j < 4; ++j)
+            if (overlaps(outs[i].p, outs[i].n, outs[j].p, outs[j].n)) return FA_ERR_ALIAS;
+    }
+
+    fa::BwdArgs a{Q, K, V, O, dO, LSE, Dws, dQ, dK, dV, bh, H, Hkv, N, (int)d, dtype, scale};
+    return fa::launch_backward(a, stream) == hipSuccess ? FA_OK : FA_ERR_LAUNCH;
 }
 
 extern "C" const char* fa_status_string(int status) {

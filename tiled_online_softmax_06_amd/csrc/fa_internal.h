@@ -22,6 +22,29 @@ struct FwdArgs {
     float scale;     // finite
 };
 
+struct BwdArgs {
+    const void* q;
+    const void* k;
+    const void* v;
+    const void* o;
+    const void* dout;
+    const float* lse;
+    float* dws;      // B * H * N floats: rowsum(dO * O)
+    void* dq;
+    void* dk;
+    void* dv;
+    int64_t bh;      // B * H
+    int64_t h;       // H
+    int64_t hkv;     // K/V heads (divides H)
+    int64_t n;
+    int d;
+    int dtype;       // fp16 or bf16
+    float scale;
+};
+
+// Launches the backward kernels (row dots, dQ, dK/dV) on `stream`.
+hipError_t launch_backward(const BwdArgs& a, hipStream_t stream);
+
 // Launches the forward kernel matching (dtype, d) on `stream`.
 // Preconditions (checked by the caller): shapes valid and non-empty,
 // pointers non-null, aligned and non-overlapping outputs.

@@ -36,6 +36,9 @@ def load_library():
         lib.fa_forward_gqa.argtypes = [ctypes.c_void_p] * 5 + [ctypes.c_int64] * 5 + [
             ctypes.c_float, ctypes.c_int, ctypes.c_void_p]
         lib.fa_forward_gqa.restype = ctypes.c_int
+        lib.fa_backward.argtypes = [ctypes.c_void_p] * 10 + [ctypes.c_int64] * 5 + [
+            ctypes.c_float, ctypes.c_int, ctypes.c_void_p]
+        lib.fa_backward.restype = ctypes.c_int
         lib.fa_status_string.argtypes = [ctypes.c_int]
         lib.fa_status_string.restype = ctypes.c_char_p
         lib.fa_version.argtypes = []
@@ -92,3 +95,52 @@ def forward(q, k, v, scale: float | None = None):
     lse = torch.empty(q.shape[:3], dtype=torch.float32, device=q.device)
     forward_into(q, k, v, o, lse, scale)
     return o, lse
+
+
+def backward_into(q, k, v, o, do, lse, dq, dk, dv, dws, scale: float | None = None, stream=None) -> None:
+    """Gradients of forward(q, k, v) for upstream gradient do, written in place.
+
+    q, o, do, dq: (B, H, N, d); k, v, dk, dv: (B, H_kv, N, d); lse: the
+    forward's (B, H, N) float32 LSE; dws: (B, H, N) float32 workspace (gets
+    rowsum(do * o)).  fp16 / bf16 only."""
+    lib = load_library()
+    for name, t in (("q", q), ("k", k), ("v", v), ("o", o), ("do", do), ("lse", lse), ("dq", dq),
+                    ("dk", dk), ("dv", dv), ("dws", dws)):
+        if not t.is_cuda:
+            raise ValueError(f"{name} must be a GPU tensor")
+        if not t.is_contiguous():
+            raise ValueError(f"{name} must be contiguous")
+    if q.dtype not in (torch.float16, torch.bfloat16):
+        raise ValueError("backward supports float16 and bfloat16")
+    for name, t in (("k", k), ("v", v), ("o", o), ("do", do), ("dq", dq), ("dk", dk), ("dv", dv)):
+        if t.dtype != q.dtype:
+            raise ValueError(f"{name} must have q's dtype")
+    if lse.dtype != torch.float32 or dws.dtype != torch.float32:
+        raise ValueError("lse and dws must be float32")
+    B, H, N, d = q.shape
+    Hkv = k.shape[1]
+    if (o.shape != q.shape or do.shape != q.shape or dq.shape != q.shape or v.shape != k.shape
+            or dk.shape != k.shape or dv.shape != k.shape or k.shape[0] != B or k.shape[2:] != q.shape[2:]
+            or tuple(lse.shape) != (B, H, N) or tuple(dws.shape) != (B, H, N)):
+        raise ValueError("shape mismatch")
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    if stream is None:
+        stream = torch.cuda.current_stream(q.device)
+    handle = stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
+    with torch.cuda.device(q.device):
+        rc = lib.fa_backward(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), do.data_ptr(),
+                             lse.data_ptr(), dws.data_ptr(), dq.data_ptr(), dk.data_ptr(), dv.data_ptr(),
+                             B, H, Hkv, N, d, float(scale), FA_DTYPE[q.dtype], handle)
+    if rc != 0:
+        raise RuntimeError(f"fa_backward failed: {status_string(rc)} ({rc})")
+
+
+def backward(q, k, v, o, do, lse, scale: float | None = None):
+    """Returns (dq, dk, dv) for the forward outputs (o, lse) of (q, k, v)."""
+    dq = torch.empty_like(q)
+    dk = torch.empty_like(k)
+    dv = torch.empty_like(v)
+    dws = torch.empty(q.shape[:3], dtype=torch.float32, device=q.device)
+    backward_into(q, k, v, o, do, lse, dq, dk, dv, dws, scale)
+    return dq, dk, dv

@@ -20,6 +20,10 @@ float32 draws are rounded to the storage dtype with round-to-nearest-even
 upcast exactly to float64, to the oracle.  The "xlong" workload is checked on
 256 distinct flat (b, h, n) query indices drawn without replacement by
 ``default_rng(2005)`` and sorted.
+
+Backward pass: the upstream gradient dO of workload k is N(0, 1) of shape
+(B, H, N, d) from ``default_rng(3000+k)``, rounded to the storage dtype the
+same way; ``random_grad`` draws one for any shape and seed.
 """
 from __future__ import annotations
 
@@ -115,6 +119,18 @@ def random_qkv(shape, dtype: str, seed: int, sigma: float = 1.0, kv_heads: int |
             x *= np.float32(sigma)
         out.append(torch.from_numpy(x).to(DTYPES[dtype]).contiguous())
     return tuple(out)
+
+
+def make_grad(w: Workload, seed: int | None = None):
+    """The workload's upstream gradient dO: N(0, 1), (B, H, N, d), its dtype."""
+    return random_grad((w.B, w.H, w.N, w.d), w.dtype, 3000 + w.index if seed is None else seed)
+
+
+def random_grad(shape, dtype: str, seed: int):
+    """Seeded N(0, 1) tensor of the given shape rounded to ``dtype``."""
+    rng = np.random.default_rng(seed)
+    x = rng.standard_normal(tuple(shape), dtype=np.float32)
+    return torch.from_numpy(x).to(DTYPES[dtype]).contiguous()
 
 
 def sample_rows(w: Workload, count: int | None = None, seed: int = 2005) -> np.ndarray:
