@@ -2,12 +2,19 @@
 """Attention forward benchmark on one MI355X.
 
     python bench.py [--steps K] [--warmup W] [--workload long] [--no-cpu-baseline]
+                    [--op forward|backward] [--seq-len N] [--kv-heads G]
 
 One step = one fa_forward launch over the whole workload (every query row of
 every head) with Q, K, V, O and LSE already resident in HBM.  Prints one JSON
 line: TFLOP/s counted as 4*B*H*N^2*d (non-causal), the kernel's roofline
 against the MFMA peak, and the CPU oracle timed on a bounded sample of the
 same workload on this host's cores.
+
+--op backward times one fa_backward call instead (its three kernels, with
+O and LSE from one forward launch made before timing) and counts
+10*B*H*N^2*d: the five N x N x d products of the gradient (S, dP, dV, dQ,
+dK), recomputation of S included, as is usual for attention backward.
+--seq-len replaces the workload's N (same seeds and other sizes).
 """
 from __future__ import annotations
 
@@ -23,14 +30,16 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, HERE)
 
 METRIC = "attention fwd TFLOP/s (4·B·H·N²·d) bf16 at 1 GPU + % of MFMA peak"
+METRIC_BWD = "attention bwd TFLOP/s (10·B·H·N²·d) at 1 GPU + % of MFMA peak"
 # MI355X published dense matrix peaks (TFLOP/s) and HBM bandwidth (GB/s).
 PEAK_TFLOPS = {"bf16": 2500.0, "fp16": 2500.0, "fp32": 157.3}
 PEAK_HBM_GBS = 8000.0
 KERNEL_SOURCE = os.path.join(HERE, "tiled_online_softmax_06_amd", "csrc", "flash_fwd.hip")
+BWD_SOURCE = os.path.join(HERE, "tiled_online_softmax_06_amd", "csrc", "flash_bwd.hip")
 
 
-def kernel_hash() -> str:
-    with open(KERNEL_SOURCE, "rb") as f:
+def kernel_hash(path: str = KERNEL_SOURCE) -> str:
+    with open(path, "rb") as f:
         return hashlib.sha256(f.read()).hexdigest()[:16]
 
 
@@ -52,6 +61,42 @@ def traffic_record(workload: str):
     if rec.get("kernel_sha256_16") != kernel_hash():
         return None
     return rec
+
+
+def cpu_baseline_backward(w, q, k, v, do, heads: int, workers: int):
+    """The backward oracle, untuned, on a bounded sample: the first `heads`
+    (b, h) heads of the workload (whole heads: every query and key), one head
+    per worker thread with one BLAS thread each."""
+    from concurrent.futures import ThreadPoolExecutor
+
+    import numpy as np
+    from threadpoolctl import threadpool_limits
+
+    import oracle
+    from tiled_online_softmax_06_amd import inputs
+
+    g = w.H // k.shape[1]
+    heads = max(1, min(heads, w.B * w.H))
+    scale = float(np.float32(w.scale))
+    qf, dof = (t.reshape(1, w.B * w.H, w.N, w.d) for t in (q, do))
+    kf, vf = (t.reshape(1, -1, w.N, w.d) for t in (k, v))
+
+    def job(h):
+        sl = (slice(0, 1), slice(h, h + 1))
+        kv = (slice(0, 1), slice(h // g, h // g + 1))
+        return oracle.attention_bwd_ref(inputs.to_float64(qf[sl]), inputs.to_float64(kf[kv]),
+                                        inputs.to_float64(vf[kv]), inputs.to_float64(dof[sl]), scale)
+
+    with threadpool_limits(1):
+        t0 = time.perf_counter()
+        with ThreadPoolExecutor(max_workers=workers) as ex:
+            list(ex.map(job, range(heads)))
+        dt = time.perf_counter() - t0
+    flops = 10 * heads * w.N * w.N * w.d
+    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": min(workers, heads), "kind": "oracle",
+            "sample": f"first {heads} of {w.B * w.H} heads, every query and key "
+                      f"({flops / 1e9:.1f} GFLOP counted as 10*N^2*d per head, float64)",
+            "seconds": round(dt, 3)}
 
 
 def cpu_baseline(w, q, k, v, heads: int, chunk: int, workers: int, gpu_out=None):
@@ -112,6 +157,8 @@ def main():
                     help="K/V heads for a grouped-query run (0: one per query head)")
     ap.add_argument("--cpu-heads", type=int, default=0,
                     help="heads the CPU oracle computes in full (0: every head of the workload)")
+    ap.add_argument("--op", choices=("forward", "backward"), default="forward")
+    ap.add_argument("--seq-len", type=int, default=0, help="override the workload's N (0: keep it)")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="also run a plain 512 MiB device copy (for HBM counter calibration)")
     args = ap.parse_args()
@@ -127,7 +174,15 @@ def main():
 
     from tiled_online_softmax_06_amd import fa, inputs
 
+    import dataclasses
+
     w = inputs.WORKLOADS[args.workload]
+    if args.seq_len > 0:
+        w = dataclasses.replace(w, N=args.seq_len)
+    backward = args.op == "backward"
+    if backward and w.dtype == "fp32":
+        print("the backward kernels take fp16 / bf16 inputs", file=sys.stderr)
+        sys.exit(2)
     dev = torch.device("cuda:0")
     kv_heads = args.kv_heads or w.H
     if w.H % kv_heads:
@@ -141,6 +196,16 @@ def main():
 
     def step():
         fa.forward_into(qd, kd, vd, o, lse, w.scale, stream=stream)
+
+    if backward:
+        do = inputs.make_grad(w)
+        dod = do.to(dev)
+        step()
+        dq, dk, dv = torch.empty_like(qd), torch.empty_like(kd), torch.empty_like(vd)
+        dws = torch.empty(qd.shape[:3], dtype=torch.float32, device=dev)
+
+        def step():  # noqa: F811
+            fa.backward_into(qd, kd, vd, o, dod, lse, dq, dk, dv, dws, w.scale, stream=stream)
 
     if args.calibrate_copy:
         src = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
@@ -162,6 +227,8 @@ def main():
     ms = start.elapsed_time(end) / max(args.steps, 1)
 
     flops = w.flops
+    if backward:
+        flops = 10 * w.B * w.H * w.N * w.N * w.d
     tflops = flops / (ms * 1e-3) / 1e12
     props = torch.cuda.get_device_properties(dev)
     peak = PEAK_TFLOPS[w.dtype]
@@ -169,13 +236,17 @@ def main():
             "frac": round(tflops / peak, 4), "traffic": None,
             "kernel": kernel_name(w),
             "avg_launch_ms": round(ms, 5)}
-    rec = traffic_record(w.name)
+    if backward:
+        roof["kernel"] = (f"flash_bwd_dot + flash_bwd_dq + flash_bwd_dkdv <{w.dtype}, d={w.d}> "
+                          "(one fa_backward call)")
+        roof["avg_launch_ms_note"] = "the three kernels of one call, stream order"
+    rec = None if backward or args.seq_len else traffic_record(w.name)
     if rec is not None:
         roof["traffic"] = rec["hbm_bytes_per_launch"]
         roof["traffic_note"] = rec.get("note", "")
 
     result = {
-        "metric": METRIC,
+        "metric": METRIC if not backward else METRIC_BWD,
         "value": round(tflops, 2),
         "unit": "TFLOP/s",
         "n_gpus": 1,
@@ -194,9 +265,15 @@ def main():
         "roofline": roof,
         "device": {"name": props.name, "cu": props.multi_processor_count,
                    "gcn_arch": getattr(props, "gcnArchName", "")},
-        "kernel_sha256_16": kernel_hash(),
+        "kernel_sha256_16": kernel_hash(BWD_SOURCE if backward else KERNEL_SOURCE),
     }
-    if not args.no_cpu_baseline:
+    if backward:
+        result["op"] = "backward"
+        result["config"]["op"] = "backward"
+    if not args.no_cpu_baseline and backward:
+        workers = max(1, min(16, len(os.sched_getaffinity(0))))
+        result["cpu_baseline"] = cpu_baseline_backward(w, q, k, v, do, args.cpu_heads or min(8, workers), workers)
+    elif not args.no_cpu_baseline:
         workers = max(1, min(16, len(os.sched_getaffinity(0))))
         chunk = 512 if w.N >= 4096 else max(64, w.N // 4)
         result["cpu_baseline"] = cpu_baseline(w, q, k, v, args.cpu_heads, chunk, workers,
