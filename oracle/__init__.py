@@ -7,6 +7,7 @@ from .attention_ref import (  # noqa: F401
     empty_state,
     finalize_state,
     kv_head,
+    merge_partials,
     merge_states,
     online_blocked_ref,
 )

@@ -151,6 +151,31 @@ def finalize_state(st: State):
     return st.o / st.l[:, None], st.m + np.log(st.l)
 
 
+def merge_partials(o_parts, lse_parts):
+    """Merge normalised partial results computed over disjoint key ranges.
+
+    o_parts (S, R, dv) and lse_parts (S, R): part s holds, for R query rows,
+    the attention output and LSE against key range s alone; an empty range
+    is O = 0, LSE = -inf.  A part is the online-softmax triple
+    (m, l, O~) = (LSE_s, 1, O_s) (the normaliser absorbed into m: O_s = O~ / l,
+    LSE_s = m + ln l), so the parts fold with the merge of [ES] formula 2
+    (merge_states, R1) and finalise as usual.  Rows whose parts are all empty
+    have no softmax; they come back as O = 0, LSE = -inf.
+    """
+    o_parts, lse_parts = _f64(o_parts), _f64(lse_parts)
+    S, R = lse_parts.shape
+    st = empty_state(R, o_parts.shape[-1])
+    for s in range(S):
+        live = np.isfinite(lse_parts[s])
+        st = merge_states(st, State(lse_parts[s], live.astype(np.float64), np.where(live[:, None], o_parts[s], 0.0)))
+    o = np.zeros_like(st.o)
+    lse = np.full(R, -np.inf)
+    ok = st.l > 0
+    if ok.any():
+        o[ok], lse[ok] = finalize_state(State(st.m[ok], st.l[ok], st.o[ok]))
+    return o, lse
+
+
 def online_blocked_ref(q, k, v, scale, bounds):
     """Running online softmax over key blocks, for one head.
 

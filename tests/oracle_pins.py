@@ -354,6 +354,38 @@ def pin_merge_with_sharp_maxima(orc):
     _close(lse, [700.0], what="empty-state identity LSE")
 
 
+def pin_partials_reproduce_full_attention(orc):
+    """Key ranges (some empty) computed on their own by library attention,
+    then merged as (O_s, LSE_s) pairs, give library attention over all keys;
+    the all-empty row is O = 0, LSE = -inf.  One head has its partial LSEs
+    near 750, where exp(LSE) overflows float64 unless the merge shifts by
+    the max first."""
+    r = _rng(31)
+    cases = [(q, k, v, 0.6) for q, k, v in _tiny_heads()]
+    q0 = np.array([[1.0], [-0.5]])
+    k0 = np.array([[760.0], [745.0], [752.0], [0.0]])
+    cases.append((q0, k0, np.array([[1.0], [-2.0], [0.5], [4.0]]), 1.0))
+    for q, k, v, s in cases:
+        n = k.shape[0]
+        o_ref, lse_ref = _library_head(q, k, v, s)
+        for _ in range(6):
+            cuts = sorted(r.integers(0, n + 1, size=int(r.integers(1, 4))))
+            edges = [0] + list(cuts) + [n]
+            o_p, l_p = [], []
+            for a, b in zip(edges[:-1], edges[1:]):
+                if b > a:
+                    o_s, l_s = _library_head(q, k[a:b], v[a:b], s)
+                else:
+                    o_s, l_s = np.zeros((q.shape[0], v.shape[1])), np.full(q.shape[0], -np.inf)
+                o_p.append(o_s)
+                l_p.append(l_s)
+            o, lse = orc.merge_partials(np.stack(o_p), np.stack(l_p))
+            _close(o, o_ref, tol=1e-11, what=f"merged partials O, edges {edges}")
+            _close(lse, lse_ref, tol=1e-11, what=f"merged partials LSE, edges {edges}")
+    o, lse = orc.merge_partials(np.zeros((3, 2, 5)), np.full((3, 2), -np.inf))
+    assert np.all(o == 0.0) and np.all(lse == -np.inf), "all-empty rows: O = 0, LSE = -inf"
+
+
 # ---------------------------------------------------------------------------
 # The backward pass (gradients of the definition, S and P recomputed)
 # ---------------------------------------------------------------------------
@@ -433,6 +465,7 @@ BLOCKED_PINS = [
     pin_every_contiguous_partition,
     pin_random_merge_trees,
     pin_merge_with_sharp_maxima,
+    pin_partials_reproduce_full_attention,
 ]
 
 ALL_PINS = DEFINITION_PINS + BLOCKED_PINS + BACKWARD_PINS

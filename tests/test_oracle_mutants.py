@@ -172,9 +172,20 @@ def _bwd_variant(no_d=False, dq_no_scale=False, dk_from_p=False, overwrite=False
     return bwd
 
 
+def _partials_unnormalised(o_parts, lse_parts):
+    m = np.max(lse_parts, axis=0)
+    w = np.exp(lse_parts - m)
+    return np.einsum("sr,srd->rd", w, o_parts), m + np.log(w.sum(axis=0))
+
+
+def _partials_no_max_shift(o_parts, lse_parts):
+    w = np.exp(lse_parts)
+    return np.einsum("sr,srd->rd", w, o_parts) / w.sum(axis=0)[:, None], np.log(w.sum(axis=0))
+
+
 ORIG = {n: getattr(ref, n) for n in ("attention_ref", "_head_rows", "_factor", "merge_states",
                                      "online_blocked_ref", "finalize_state", "block_state", "kv_head",
-                                     "attention_bwd_ref")}
+                                     "attention_bwd_ref", "merge_partials")}
 
 MUTANTS = {f"rows:{k}": {"_head_rows": f} for k, f in ROW_MUTANTS.items()}
 MUTANTS.update({
@@ -188,6 +199,8 @@ MUTANTS.update({
     "online:block_off_by_one": {"online_blocked_ref": _online_block_off_by_one},
     "finalize:lse_without_max": {"finalize_state": _finalize_lse_no_max},
     "gqa:kv_head_modulo": {"kv_head": _kv_head_modulo},
+    "partials:weights_unnormalised": {"merge_partials": _partials_unnormalised},
+    "partials:no_max_shift": {"merge_partials": _partials_no_max_shift},
     "bwd:no_rowsum_term": {"attention_bwd_ref": _bwd_variant(no_d=True)},
     "bwd:dq_without_scale": {"attention_bwd_ref": _bwd_variant(dq_no_scale=True)},
     "bwd:dk_from_p": {"attention_bwd_ref": _bwd_variant(dk_from_p=True)},
@@ -199,7 +212,8 @@ MUTANTS.update({
 def _module_view():
     return types.SimpleNamespace(**{n: getattr(ref, n) for n in
                                     ("attention_ref", "block_state", "empty_state", "merge_states",
-                                     "finalize_state", "online_blocked_ref", "State", "attention_bwd_ref")})
+                                     "finalize_state", "online_blocked_ref", "State", "attention_bwd_ref",
+                                     "merge_partials")})
 
 
 @pytest.mark.parametrize("name", sorted(MUTANTS))
