@@ -14,6 +14,10 @@ same workload on this host's cores.
 O and LSE from one forward launch made before timing) and counts
 10*B*H*N^2*d: the five N x N x d products of the gradient (S, dP, dV, dQ,
 dK), recomputation of S included, as is usual for attention backward.
+--op split times one fa_forward_split call (forward kernel over key ranges
+plus the merge kernel; workspace allocated before timing) with --splits
+ranges (0: the library's suggestion), counts 4*B*H*N^2*d like the forward,
+and also reports the unsplit forward on the same inputs.
 --seq-len replaces the workload's N (same seeds and other sizes).
 """
 from __future__ import annotations
@@ -157,7 +161,8 @@ def main():
                     help="K/V heads for a grouped-query run (0: one per query head)")
     ap.add_argument("--cpu-heads", type=int, default=0,
                     help="heads the CPU oracle computes in full (0: every head of the workload)")
-    ap.add_argument("--op", choices=("forward", "backward"), default="forward")
+    ap.add_argument("--op", choices=("forward", "backward", "split"), default="forward")
+    ap.add_argument("--splits", type=int, default=0, help="key ranges for --op split (0: suggested)")
     ap.add_argument("--seq-len", type=int, default=0, help="override the workload's N (0: keep it)")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="also run a plain 512 MiB device copy (for HBM counter calibration)")
@@ -207,6 +212,31 @@ def main():
         def step():  # noqa: F811
             fa.backward_into(qd, kd, vd, o, dod, lse, dq, dk, dv, dws, w.scale, stream=stream)
 
+    split = args.op == "split"
+    unsplit_ms = None
+    if split:
+        splits = args.splits or fa.split_suggest(w.B, w.H, w.N, w.d, qd.dtype)
+        ws = torch.empty(max(fa.split_workspace_bytes(w.B, w.H, w.N, w.d, splits), 16), dtype=torch.uint8,
+                         device=dev)
+
+        def time_it(fn, steps):
+            for _ in range(args.warmup):
+                fn()
+            torch.cuda.synchronize()
+            t0 = torch.cuda.Event(enable_timing=True)
+            t1 = torch.cuda.Event(enable_timing=True)
+            t0.record(stream)
+            for _ in range(steps):
+                fn()
+            t1.record(stream)
+            torch.cuda.synchronize()
+            return t0.elapsed_time(t1) / max(steps, 1)
+
+        unsplit_ms = time_it(step, args.steps)
+
+        def step():  # noqa: F811
+            fa.forward_split_into(qd, kd, vd, o, lse, ws, splits, w.scale, stream=stream)
+
     if args.calibrate_copy:
         src = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
         dst = torch.empty_like(src)
@@ -236,11 +266,14 @@ def main():
             "frac": round(tflops / peak, 4), "traffic": None,
             "kernel": kernel_name(w),
             "avg_launch_ms": round(ms, 5)}
+    if split:
+        roof["kernel"] = f"{kernel_name(w)} over {splits} key ranges + fa_merge_rows (one fa_forward_split call)"
+        roof["avg_launch_ms_note"] = "the two kernels of one call, stream order"
     if backward:
         roof["kernel"] = (f"flash_bwd_dot + flash_bwd_dq + flash_bwd_dkdv <{w.dtype}, d={w.d}> "
                           "(one fa_backward call)")
         roof["avg_launch_ms_note"] = "the three kernels of one call, stream order"
-    rec = None if backward or args.seq_len else traffic_record(w.name)
+    rec = None if backward or split or args.seq_len else traffic_record(w.name)
     if rec is not None:
         roof["traffic"] = rec["hbm_bytes_per_launch"]
         roof["traffic_note"] = rec.get("note", "")
@@ -270,7 +303,17 @@ def main():
     if backward:
         result["op"] = "backward"
         result["config"]["op"] = "backward"
-    if not args.no_cpu_baseline and backward:
+    if split:
+        result["op"] = "split"
+        result["config"]["op"] = "split"
+        result["config"]["splits"] = splits
+        result["unsplit"] = {"ms_per_step": round(unsplit_ms, 5),
+                             "value": round(flops / (unsplit_ms * 1e-3) / 1e12, 2)}
+    if not args.no_cpu_baseline and split:
+        workers = max(1, min(16, len(os.sched_getaffinity(0))))
+        result["cpu_baseline"] = cpu_baseline(w, q, k, v, args.cpu_heads, 512, workers,
+                                              gpu_out=(o.cpu(), lse.cpu()))
+    elif not args.no_cpu_baseline and backward:
         workers = max(1, min(16, len(os.sched_getaffinity(0))))
         result["cpu_baseline"] = cpu_baseline_backward(w, q, k, v, do, args.cpu_heads or min(8, workers), workers)
     elif not args.no_cpu_baseline:

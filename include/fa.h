@@ -46,7 +46,8 @@ typedef enum {
     FA_ERR_MISALIGNED = 5,            /* Q/K/V/O not 16-byte or LSE not 4-byte aligned  */
     FA_ERR_ALIAS = 6,                 /* O or LSE overlaps an input or each other       */
     FA_ERR_BAD_SCALE = 7,             /* scale is NaN or infinite                       */
-    FA_ERR_LAUNCH = 8                 /* the HIP kernel launch itself failed            */
+    FA_ERR_LAUNCH = 8,                /* the HIP kernel launch itself failed            */
+    FA_ERR_WORKSPACE = 9              /* workspace NULL or smaller than required        */
 } fa_status_t;
 
 /*
@@ -143,6 +144,69 @@ int fa_backward(const void* Q, const void* K, const void* V, const void* O, cons
                 const float* LSE, float* Dws, void* dQ, void* dK, void* dV,
                 int64_t B, int64_t H, int64_t H_kv, int64_t N, int64_t d,
                 float scale, int dtype, hipStream_t stream);
+
+/*
+ * fa_forward_split — fa_forward_gqa with the keys of every head cut into
+ * ranges processed by separate workgroups, then merged.  For few heads and
+ * long sequences (B*H*ceil(N/256) below the number of compute units) this
+ * fills the GPU that one query tile per workgroup leaves idle.
+ *
+ * Each range r yields the normalised partial result of the rows against its
+ * keys alone, (O_r, LSE_r); the ranges merge by the softmax merge of the
+ * unite.ai page (section "La Matemática detrás de la Atención Flash",
+ * formula 2, normalisers restored), in log-sum-exp form:
+ *
+ *     m = max_r LSE_r,   w_r = exp(LSE_r - m)
+ *     O = sum_r w_r O_r / sum_r w_r,   LSE = m + ln sum_r w_r
+ *
+ * which is exactly the unsplit result up to rounding.  The partials are kept
+ * in float32 in the caller's workspace.
+ *
+ * splits    requested number of ranges, >= 1.  Ranges hold a whole number
+ *           of 64-key tiles and none is empty, so the count used is
+ *           ceil(N / kchunk) with kchunk = 64 * ceil(ceil(N/64) / splits),
+ *           at most `splits`.  One range runs fa_forward_gqa (no workspace
+ *           needed).
+ * workspace device, 16-byte aligned, at least fa_split_workspace_bytes(...)
+ *           bytes, overlapping no other argument; its contents on return are
+ *           the partial results (O parts (B*H, ranges, N, d) float32, then
+ *           LSE parts (B*H, ranges, N) float32).
+ * Everything else as for fa_forward_gqa.  FA_ERR_WORKSPACE: workspace NULL
+ * or too small.  Two kernels are launched in stream order.
+ */
+int fa_forward_split(const void* Q, const void* K, const void* V, void* O, float* LSE,
+                     int64_t B, int64_t H, int64_t H_kv, int64_t N, int64_t d,
+                     float scale, int dtype, int64_t splits, void* workspace,
+                     int64_t workspace_bytes, hipStream_t stream);
+
+/* Workspace bytes fa_forward_split needs for these sizes and requested
+ * splits (0 when one range results or B*H*N == 0; -1 for invalid sizes). */
+int64_t fa_split_workspace_bytes(int64_t B, int64_t H, int64_t N, int64_t d, int64_t splits);
+
+/* A split count for fa_forward_split on the MI355X's 256 compute units:
+ * the count with the fewest estimated workgroup-tile steps (waves of
+ * workgroups times tiles per range, plus the merge's memory traffic), at
+ * most 64 and keeping at least 512 keys per range; 1 when no split pays off
+ * or the sizes are invalid. */
+int64_t fa_split_suggest(int64_t B, int64_t H, int64_t N, int64_t d, int dtype);
+
+/*
+ * fa_merge — merge S normalised partial attention results per row (the
+ * merge of fa_forward_split on its own; also the combine step for keys
+ * sharded over devices, each shard having produced (O_s, LSE_s)).
+ *
+ * O_parts   device, read only, (G, S, M, d) float32: part s of row i of
+ *           group g at ((g*S + s)*M + i)*d.
+ * LSE_parts device, read only, (G, S, M) float32, natural log.  A part with
+ *           LSE = -inf has no keys and weighs 0; a row whose parts are all
+ *           -inf gets O = 0 and LSE = -inf.
+ * O         device, written, (G, M, d) of `dtype` (rounded to nearest even).
+ * LSE       device, written, (G, M) float32.
+ * S >= 1; d 64 or 128; outputs must not overlap each other or the inputs.
+ * Ownership and errors as for fa_forward; G*M == 0 returns FA_OK.
+ */
+int fa_merge(const float* O_parts, const float* LSE_parts, int64_t G, int64_t S, int64_t M,
+             int64_t d, void* O, float* LSE, int dtype, hipStream_t stream);
 
 /* Static, human-readable name of a return code ("unknown status" otherwise). */
 const char* fa_status_string(int status);

@@ -36,7 +36,8 @@ def _header_enum(name):
 
 def test_exports_every_declared_function(lib):
     funcs = _header_functions()
-    assert set(funcs) == {"fa_forward", "fa_forward_gqa", "fa_backward", "fa_status_string",
+    assert set(funcs) == {"fa_forward", "fa_forward_gqa", "fa_backward", "fa_forward_split",
+                          "fa_split_workspace_bytes", "fa_split_suggest", "fa_merge", "fa_status_string",
                           "fa_version"}
     out = subprocess.run(["nm", "-D", "--defined-only", lib._name], capture_output=True, text=True).stdout
     exported = set(re.findall(r" T (\w+)$", out, flags=re.M))
@@ -162,3 +163,88 @@ def test_backward_error_codes(lib):
     assert call_bwd(lib, dws=A + 448 * MB) == codes["FA_ERR_ALIAS"]            # workspace == dQ
     assert call_bwd(lib, q=None, k=None, v=None, o=None, do=None, lse=None, dws=None, dq=None,
                     dk=None, dv=None, N=0) == 0
+
+
+def _split_lib(lib):
+    lib.fa_forward_split.argtypes = [ctypes.c_void_p] * 5 + [ctypes.c_int64] * 5 + [
+        ctypes.c_float, ctypes.c_int, ctypes.c_int64, ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p]
+    lib.fa_split_workspace_bytes.argtypes = [ctypes.c_int64] * 5
+    lib.fa_split_workspace_bytes.restype = ctypes.c_int64
+    lib.fa_split_suggest.argtypes = [ctypes.c_int64] * 4 + [ctypes.c_int]
+    lib.fa_split_suggest.restype = ctypes.c_int64
+    lib.fa_merge.argtypes = [ctypes.c_void_p] * 2 + [ctypes.c_int64] * 4 + [
+        ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int, ctypes.c_void_p]
+    return lib
+
+
+def test_split_workspace_bytes(lib):
+    """Ranges are whole 64-key tiles and never empty: ceil(N / kchunk) ranges
+    with kchunk = 64 ceil(ceil(N / 64) / splits); bytes = B H ranges N (d+1) 4."""
+    _split_lib(lib)
+    for B, H, N, d, splits in ((1, 2, 16384, 128, 2), (1, 1, 1000, 64, 5), (1, 1, 100, 64, 5), (2, 3, 4097, 128, 7),
+                               (1, 1, 64, 64, 4), (3, 1, 1, 128, 9), (1, 1, 8192, 64, 1)):
+        tiles = -(-N // 64)
+        s_ = min(splits, tiles)
+        kchunk = 64 * -(-tiles // s_)
+        ranges = -(-N // kchunk)
+        want = 0 if ranges == 1 else B * H * ranges * N * (d + 1) * 4
+        assert lib.fa_split_workspace_bytes(B, H, N, d, splits) == want, (B, H, N, d, splits)
+    assert lib.fa_split_workspace_bytes(1, 1, 1000, 64, 0) == -1
+    assert lib.fa_split_workspace_bytes(-1, 1, 1000, 64, 2) == -1
+    assert lib.fa_split_workspace_bytes(1 << 40, 1 << 20, 1 << 10, 64, 8) == -1      # overflow
+    assert lib.fa_split_workspace_bytes(0, 4, 1000, 64, 4) == 0
+
+
+def test_split_suggest(lib):
+    _split_lib(lib)
+    assert lib.fa_split_suggest(2, 16, 8192, 128, 2) == 1       # 1024 workgroups already
+    assert lib.fa_split_suggest(1, 2, 16384, 128, 2) == 2       # 128 workgroups -> 256
+    assert lib.fa_split_suggest(1, 1, 8192, 128, 2) == 8        # 32 -> 256, 1024 keys per range
+    assert lib.fa_split_suggest(1, 1, 1024, 128, 2) == 2        # capped at 512 keys per range
+    assert lib.fa_split_suggest(1, 1, 500, 64, 1) == 1          # too short to split
+    assert lib.fa_split_suggest(1, 1, 8192, 96, 2) == 1         # unsupported d
+
+
+def call_split(lib, q=A, k=A + 64 * MB, v=A + 128 * MB, o=A + 192 * MB, lse=A + 256 * MB, ws=A + 320 * MB,
+               ws_bytes=1 << 30, B=1, H=2, Hkv=2, N=1000, d=64, splits=4, scale=0.125, dtype=2):
+    return lib.fa_forward_split(q, k, v, o, lse, B, H, Hkv, N, d, scale, dtype, splits, ws, ws_bytes, None)
+
+
+def test_split_error_codes(lib):
+    codes = _header_enum("fa_status_t")
+    _split_lib(lib)
+    need = lib.fa_split_workspace_bytes(1, 2, 1000, 64, 4)
+    assert call_split(lib, splits=0) == codes["FA_ERR_BAD_SHAPE"]
+    assert call_split(lib, Hkv=3) == codes["FA_ERR_BAD_SHAPE"]
+    assert call_split(lib, d=80) == codes["FA_ERR_UNSUPPORTED_HEAD_DIM"]
+    assert call_split(lib, scale=math.nan) == codes["FA_ERR_BAD_SCALE"]
+    assert call_split(lib, ws=None) == codes["FA_ERR_WORKSPACE"]
+    assert call_split(lib, ws_bytes=need - 1) == codes["FA_ERR_WORKSPACE"]
+    assert call_split(lib, ws=A + 320 * MB + 4) == codes["FA_ERR_MISALIGNED"]
+    assert call_split(lib, ws=A + 192 * MB - 1024) == codes["FA_ERR_ALIAS"]     # workspace runs into O
+    assert call_split(lib, ws=A + 16) == codes["FA_ERR_ALIAS"]                  # workspace inside Q
+    assert call_split(lib, o=A + 64) == codes["FA_ERR_ALIAS"]                   # the forward's own checks
+    assert call_split(lib, q=None) == codes["FA_ERR_NULL_POINTER"]
+    assert call_split(lib, N=0, q=None, k=None, v=None, o=None, lse=None, ws=None) == 0
+
+
+def call_merge(lib, op=A, lp=A + 256 * MB, G=2, S=3, M=100, d=64, o=A + 512 * MB, lse=A + 768 * MB, dtype=2):
+    return lib.fa_merge(op, lp, G, S, M, d, o, lse, dtype, None)
+
+
+def test_merge_error_codes(lib):
+    codes = _header_enum("fa_status_t")
+    _split_lib(lib)
+    assert call_merge(lib, S=0) == codes["FA_ERR_BAD_SHAPE"]
+    assert call_merge(lib, G=-1) == codes["FA_ERR_BAD_SHAPE"]
+    assert call_merge(lib, G=1 << 40, M=1 << 30) == codes["FA_ERR_BAD_SHAPE"]
+    assert call_merge(lib, d=32) == codes["FA_ERR_UNSUPPORTED_HEAD_DIM"]
+    assert call_merge(lib, dtype=5) == codes["FA_ERR_UNSUPPORTED_DTYPE"]
+    for field in ("op", "lp", "o", "lse"):
+        assert call_merge(lib, **{field: None}) == codes["FA_ERR_NULL_POINTER"], field
+    assert call_merge(lib, op=A + 4) == codes["FA_ERR_MISALIGNED"]
+    assert call_merge(lib, lse=A + 768 * MB + 2) == codes["FA_ERR_MISALIGNED"]
+    assert call_merge(lib, o=A + 1024) == codes["FA_ERR_ALIAS"]                 # O inside the O parts
+    assert call_merge(lib, lse=A + 512 * MB + 64) == codes["FA_ERR_ALIAS"]      # LSE inside O
+    assert call_merge(lib, lse=A + 256 * MB) == codes["FA_ERR_ALIAS"]           # LSE on the LSE parts
+    assert call_merge(lib, M=0, op=None, lp=None, o=None, lse=None) == 0

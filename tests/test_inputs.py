@@ -7,7 +7,8 @@ from tiled_online_softmax_06_amd import inputs
 
 def test_workload_table():
     w = inputs.WORKLOADS
-    assert [x.index for x in w.values()] == [1, 2, 3, 4, 5]
+    assert [x.index for x in w.values()] == [1, 2, 3, 4, 5, 6]
+    assert (w["fewheads"].B, w["fewheads"].H, w["fewheads"].N, w["fewheads"].d) == (1, 2, 16384, 128)
     assert (w["long"].B, w["long"].H, w["long"].N, w["long"].d, w["long"].dtype) == (2, 16, 8192, 128, "bf16")
     assert w["long"].flops == 2 ** 40
     assert w["xlong"].flops == 2 ** 44

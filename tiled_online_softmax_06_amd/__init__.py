@@ -5,4 +5,17 @@ computed tile by tile with a running row max and normaliser.
 library ``libfa.so`` (see include/fa.h); every step of the computation runs
 in its HIP kernels.  ``inputs`` builds the seeded synthetic workloads.
 """
-from .fa import backward, backward_into, forward, forward_into, library_path, load_library  # noqa: F401
+from .fa import (  # noqa: F401
+    backward,
+    backward_into,
+    forward,
+    forward_into,
+    forward_split,
+    forward_split_into,
+    library_path,
+    load_library,
+    merge,
+    merge_into,
+    split_suggest,
+    split_workspace_bytes,
+)

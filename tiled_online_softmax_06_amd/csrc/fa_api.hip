@@ -20,11 +20,13 @@ bool mul_ok(int64_t x, int64_t y, int64_t* out) {
     return true;
 }
 
-}  // namespace
+// Argument checks shared by the forward entry points.  Returns FA_OK with
+// *empty set when B*H*N == 0 (nothing to launch).
+struct FwdSizes { int64_t bh, rows, bytes, kvbytes, lbytes; bool empty; };
 
-extern "C" int fa_forward_gqa(const void* Q, const void* K, const void* V, void* O, float* LSE,
-                              int64_t B, int64_t H, int64_t Hkv, int64_t N, int64_t d,
-                              float scale, int dtype, hipStream_t stream) {
+int check_forward(const void* Q, const void* K, const void* V, const void* O, const float* LSE,
+                  int64_t B, int64_t H, int64_t Hkv, int64_t N, int64_t d, float scale, int dtype,
+                  FwdSizes* sz) {
     if (B < 0 || H < 0 || N < 0 || d < 0 || Hkv < 0) return FA_ERR_BAD_SHAPE;
     if (dtype != FA_DTYPE_FP32 && dtype != FA_DTYPE_FP16 && dtype != FA_DTYPE_BF16)
         return FA_ERR_UNSUPPORTED_DTYPE;
@@ -37,6 +39,7 @@ extern "C" int fa_forward_gqa(const void* Q, const void* K, const void* V, void*
         !mul_ok(elems, esize, &bytes) || !mul_ok(B, Hkv, &bkv) || !mul_ok(bkv, N, &kvrows) ||
         !mul_ok(kvrows, d, &kvelems) || !mul_ok(kvelems, esize, &kvbytes))
         return FA_ERR_BAD_SHAPE;
+    *sz = FwdSizes{bh, rows, bytes, kvbytes, rows * 4, rows == 0};
     if (rows == 0) return FA_OK;
     // every query head needs a K/V head: Hkv >= 1 and divides H
     if (Hkv == 0 || H % Hkv != 0) return FA_ERR_BAD_SHAPE;
@@ -54,8 +57,40 @@ extern "C" int fa_forward_gqa(const void* Q, const void* K, const void* V, void*
         overlaps(LSE, lbytes, Q, bytes) || overlaps(LSE, lbytes, K, kvbytes) ||
         overlaps(LSE, lbytes, V, kvbytes) || overlaps(LSE, lbytes, O, bytes))
         return FA_ERR_ALIAS;
+    return FA_OK;
+}
 
-    fa::FwdArgs a{Q, K, V, O, LSE, bh, H, Hkv, N, (int)d, dtype, scale};
+// Key ranges for a requested split count: `*ranges` ranges of `*kchunk`
+// keys, kchunk a multiple of one 64-key tile, none empty (so at most one
+// range per tile; fewer than asked when the tiles do not divide evenly).
+void split_plan(int64_t N, int64_t splits, int64_t* ranges, int64_t* kchunk) {
+    const int64_t tiles = (N + fa::kSplitAlign - 1) / fa::kSplitAlign;
+    const int64_t s = splits < tiles ? splits : tiles;
+    const int64_t per = s > 0 ? (tiles + s - 1) / s : 1;
+    *kchunk = per * fa::kSplitAlign;
+    *ranges = N > 0 ? (N + *kchunk - 1) / *kchunk : 1;
+}
+
+// Workspace bytes for `ranges` key ranges: fp32 partial O then partial LSE.
+bool split_bytes(int64_t bh, int64_t N, int64_t d, int64_t ranges, int64_t* obytes, int64_t* lbytes) {
+    int64_t prow = 0, pel = 0;
+    if (!mul_ok(bh, ranges, &prow) || !mul_ok(prow, N, &prow) || !mul_ok(prow, d, &pel) ||
+        !mul_ok(pel, 4, obytes) || !mul_ok(prow, 4, lbytes) || *obytes > INT64_MAX - *lbytes)
+        return false;
+    return true;
+}
+
+constexpr int64_t kComputeUnits = 256;   // MI355X
+
+}  // namespace
+
+extern "C" int fa_forward_gqa(const void* Q, const void* K, const void* V, void* O, float* LSE,
+                              int64_t B, int64_t H, int64_t Hkv, int64_t N, int64_t d,
+                              float scale, int dtype, hipStream_t stream) {
+    FwdSizes sz;
+    const int st = check_forward(Q, K, V, O, LSE, B, H, Hkv, N, d, scale, dtype, &sz);
+    if (st != FA_OK || sz.empty) return st;
+    fa::FwdArgs a{Q, K, V, O, LSE, sz.bh, H, Hkv, N, (int)d, dtype, scale};
     return fa::launch_forward(a, stream) == hipSuccess ? FA_OK : FA_ERR_LAUNCH;
 }
 
@@ -63,6 +98,102 @@ extern "C" int fa_forward(const void* Q, const void* K, const void* V, void* O, 
                           int64_t B, int64_t H, int64_t N, int64_t d,
                           float scale, int dtype, hipStream_t stream) {
     return fa_forward_gqa(Q, K, V, O, LSE, B, H, H, N, d, scale, dtype, stream);
+}
+
+extern "C" int64_t fa_split_workspace_bytes(int64_t B, int64_t H, int64_t N, int64_t d, int64_t splits) {
+    if (B < 0 || H < 0 || N < 0 || d < 1 || splits < 1) return -1;
+    int64_t bh = 0, ranges = 0, kchunk = 0, ob = 0, lb = 0;
+    if (!mul_ok(B, H, &bh)) return -1;
+    if (bh == 0 || N == 0) return 0;
+    split_plan(N, splits, &ranges, &kchunk);
+    if (ranges == 1) return 0;
+    if (!split_bytes(bh, N, d, ranges, &ob, &lb)) return -1;
+    return ob + lb;
+}
+
+extern "C" int64_t fa_split_suggest(int64_t B, int64_t H, int64_t N, int64_t d, int dtype) {
+    if (B < 0 || H < 0 || N < 0 || (d != 64 && d != 128)) return 1;
+    int64_t bh = 0;
+    if (!mul_ok(B, H, &bh) || bh == 0 || N == 0 || bh > ((int64_t)1 << 40) / N) return 1;
+    const int64_t rows = fa::forward_rows_per_workgroup(dtype, (int)d);
+    const int64_t slots = kComputeUnits * fa::forward_workgroups_per_cu(dtype, (int)d);
+    const int64_t wg = bh * ((N + rows - 1) / rows);          // workgroups of one key range
+    const int64_t tiles = (N + fa::kSplitAlign - 1) / fa::kSplitAlign;
+    // Cost in 64-key tile steps of one workgroup: waves of workgroups times
+    // (tiles per range + about 2 tiles of pipeline fill and epilogue), plus,
+    // for S > 1, the merge's memory traffic (S partials read, O written) at
+    // about 12.6 MB per tile step (7 TB/s for one 1.8 us step).  Each range
+    // keeps at least 8 tiles (512 keys).
+    int64_t most = tiles / 8;
+    if (most > 64) most = 64;
+    int64_t best = 1;
+    double best_cost = 0.0;
+    for (int64_t s = 1; s <= (most > 1 ? most : 1); ++s) {
+        const int64_t waves = (wg * s + slots - 1) / slots;
+        double cost = (double)waves * (double)((tiles + s - 1) / s + 2);
+        if (s > 1) cost += (double)bh * (double)N * (double)d * (4.0 * s + 2.0) / 12.6e6;
+        if (s == 1 || cost < best_cost) {
+            best = s;
+            best_cost = cost;
+        }
+    }
+    return best;
+}
+
+extern "C" int fa_forward_split(const void* Q, const void* K, const void* V, void* O, float* LSE,
+                                int64_t B, int64_t H, int64_t Hkv, int64_t N, int64_t d,
+                                float scale, int dtype, int64_t splits, void* workspace,
+                                int64_t workspace_bytes, hipStream_t stream) {
+    if (splits < 1) return FA_ERR_BAD_SHAPE;
+    FwdSizes sz;
+    const int st = check_forward(Q, K, V, O, LSE, B, H, Hkv, N, d, scale, dtype, &sz);
+    if (st != FA_OK || sz.empty) return st;
+    int64_t ranges = 0, kchunk = 0, ob = 0, lb = 0;
+    split_plan(N, splits, &ranges, &kchunk);
+    if (ranges == 1) {
+        fa::FwdArgs a{Q, K, V, O, LSE, sz.bh, H, Hkv, N, (int)d, dtype, scale};
+        return fa::launch_forward(a, stream) == hipSuccess ? FA_OK : FA_ERR_LAUNCH;
+    }
+    if (!split_bytes(sz.bh, N, d, ranges, &ob, &lb)) return FA_ERR_BAD_SHAPE;
+    const int64_t wgs = sz.bh * ranges * ((N + fa::kMinRowsPerWorkgroup - 1) / fa::kMinRowsPerWorkgroup);
+    if (wgs > INT32_MAX) return FA_ERR_BAD_SHAPE;
+    if (!workspace || workspace_bytes < ob + lb) return FA_ERR_WORKSPACE;
+    if ((uintptr_t)workspace & 15u) return FA_ERR_MISALIGNED;
+    if (overlaps(workspace, ob + lb, Q, sz.bytes) || overlaps(workspace, ob + lb, K, sz.kvbytes) ||
+        overlaps(workspace, ob + lb, V, sz.kvbytes) || overlaps(workspace, ob + lb, O, sz.bytes) ||
+        overlaps(workspace, ob + lb, LSE, sz.lbytes))
+        return FA_ERR_ALIAS;
+    float* o_part = (float*)workspace;
+    float* lse_part = (float*)((char*)workspace + ob);
+    fa::FwdArgs a{Q, K, V, O, LSE, sz.bh, H, Hkv, N, (int)d, dtype, scale};
+    return fa::launch_forward_split(a, (int)ranges, (int)kchunk, o_part, lse_part, stream) == hipSuccess
+               ? FA_OK : FA_ERR_LAUNCH;
+}
+
+extern "C" int fa_merge(const float* O_parts, const float* LSE_parts, int64_t G, int64_t S, int64_t M,
+                        int64_t d, void* O, float* LSE, int dtype, hipStream_t stream) {
+    if (G < 0 || S < 0 || M < 0 || d < 0) return FA_ERR_BAD_SHAPE;
+    if (dtype != FA_DTYPE_FP32 && dtype != FA_DTYPE_FP16 && dtype != FA_DTYPE_BF16)
+        return FA_ERR_UNSUPPORTED_DTYPE;
+    if (d != 64 && d != 128) return FA_ERR_UNSUPPORTED_HEAD_DIM;
+    const int64_t esize = dtype == FA_DTYPE_FP32 ? 4 : 2;
+    int64_t rows = 0, prows = 0, pel = 0, pbytes = 0, el = 0, obytes = 0;
+    if (!mul_ok(G, M, &rows) || !mul_ok(rows, S, &prows) || !mul_ok(prows, d, &pel) ||
+        !mul_ok(pel, 4, &pbytes) || !mul_ok(rows, d, &el) || !mul_ok(el, esize, &obytes) ||
+        prows > INT64_MAX / 4)
+        return FA_ERR_BAD_SHAPE;
+    if (rows == 0) return FA_OK;
+    if (S < 1 || S > INT32_MAX) return FA_ERR_BAD_SHAPE;
+    if (!O_parts || !LSE_parts || !O || !LSE) return FA_ERR_NULL_POINTER;
+    if (((uintptr_t)O_parts | (uintptr_t)O) & 15u) return FA_ERR_MISALIGNED;
+    if (((uintptr_t)LSE_parts | (uintptr_t)LSE) & 3u) return FA_ERR_MISALIGNED;
+    const int64_t lbytes = rows * 4, plbytes = prows * 4;
+    if (overlaps(O, obytes, O_parts, pbytes) || overlaps(O, obytes, LSE_parts, plbytes) ||
+        overlaps(LSE, lbytes, O_parts, pbytes) || overlaps(LSE, lbytes, LSE_parts, plbytes) ||
+        overlaps(O, obytes, LSE, lbytes))
+        return FA_ERR_ALIAS;
+    return fa::launch_merge(O_parts, LSE_parts, G, S, M, (int)d, O, LSE, dtype, stream) == hipSuccess
+               ? FA_OK : FA_ERR_LAUNCH;
 }
 
 extern "C" int fa_backward(const void* Q, const void* K, const void* V, const void* O, const void* dO,
@@ -118,6 +249,7 @@ extern "C" const char* fa_status_string(int status) {
         case FA_ERR_ALIAS: return "output overlaps an input or the other output";
         case FA_ERR_BAD_SCALE: return "scale is not finite";
         case FA_ERR_LAUNCH: return "kernel launch failed";
+        case FA_ERR_WORKSPACE: return "workspace missing or smaller than required";
         default: return "unknown status";
     }
 }

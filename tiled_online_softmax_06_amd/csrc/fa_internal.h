@@ -1,5 +1,5 @@
 // Internal interface between the C-ABI layer (fa_api.hip) and the kernels
-// (flash_fwd.hip).  Not installed; include/fa.h is the public header.
+// (flash_fwd.hip, flash_bwd.hip).  Not installed; include/fa.h is the public header.
 #pragma once
 
 #include <stdint.h>
@@ -50,7 +50,27 @@ hipError_t launch_backward(const BwdArgs& a, hipStream_t stream);
 // pointers non-null, aligned and non-overlapping outputs.
 hipError_t launch_forward(const FwdArgs& a, hipStream_t stream);
 
-// Largest number of rows handled by one workgroup over all configurations;
+// Key split (one kernel launch per call, then a merge): the keys of every
+// head are cut into `splits` ranges of `kchunk` keys (kchunk a multiple of
+// kSplitAlign; the last range may be shorter; none is empty).  The forward
+// kernels write each range's normalised fp32 partial output to o_part,
+// (B*H, splits, N, d), and its LSE to lse_part, (B*H, splits, N); the merge
+// kernel then writes a.o and a.lse.
+constexpr int kSplitAlign = 64;
+hipError_t launch_forward_split(const FwdArgs& a, int splits, int kchunk, float* o_part, float* lse_part,
+                                hipStream_t stream);
+
+// Merges S normalised partial results per row: o_parts (G, S, M, d) and
+// lse_parts (G, S, M) fp32 into o (G, M, d) of `dtype` and lse (G, M).
+hipError_t launch_merge(const float* o_parts, const float* lse_parts, int64_t g, int64_t s, int64_t m, int d,
+                        void* o, float* lse, int dtype, hipStream_t stream);
+
+// Query rows per workgroup of the forward kernel chosen for (dtype, d), and
+// how many of its workgroups one CU holds at once.
+int forward_rows_per_workgroup(int dtype, int d);
+int forward_workgroups_per_cu(int dtype, int d);
+
+// Smallest number of rows handled by one workgroup over all configurations;
 // used by the caller to bound the grid size.
 constexpr int kMinRowsPerWorkgroup = 128;
 

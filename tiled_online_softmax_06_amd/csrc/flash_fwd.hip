@@ -55,11 +55,11 @@
 namespace fa {
 namespace {
 
-template <typename T, int D, int BC, int NW>
+template <typename T, int D, int BC, int NW, bool PART>
 __global__ void __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2)))
 flash_fwd_16(const T* __restrict__ Q, const T* __restrict__ K, const T* __restrict__ V,
-             T* __restrict__ O, float* __restrict__ LSE,
-             int n, int qtiles, int total, float c, int negate, int nh, int grp)
+             void* __restrict__ Out, float* __restrict__ LSE,
+             int n, int qtiles, int total, float c, int negate, int nh, int grp, int splits, int kchunk)
 {
     using M = Mfma<T>;
     constexpr int BR = 32 * NW;
@@ -87,12 +87,16 @@ flash_fwd_16(const T* __restrict__ Q, const T* __restrict__ K, const T* __restri
     const int half = lane >> 5;
 
     const int tile = xcd_tile(blockIdx.x, total);
-    const int bh = tile / qtiles;
-    const int qt = tile - bh * qtiles;
+    const int hs = tile / qtiles;            // (b H + h) splits + key range
+    const int qt = tile - hs * qtiles;
+    const int bh = hs / splits;
+    const int kbeg = (hs - bh * splits) * kchunk;
+    const int nk = min(n - kbeg, kchunk);    // keys of this range (>= 1)
     const int64_t base = (int64_t)bh * n * D;
     // K/V head of this query head: query heads h of a batch share K/V head
-    // h / grp (grp = 1: one K/V head per query head).
-    const int64_t kvbase = (int64_t)((bh / nh) * (nh / grp) + (bh % nh) / grp) * n * D;
+    // h / grp (grp = 1: one K/V head per query head); the range starts at
+    // key kbeg.
+    const int64_t kvbase = (int64_t)((bh / nh) * (nh / grp) + (bh % nh) / grp) * n * D + (int64_t)kbeg * D;
     const int qrow = qt * BR + wave * 32 + col;
 
     // Q^T as the B operand: lane (col, half) holds Q[qrow][16*kc + 8*half + 0..7]
@@ -110,9 +114,9 @@ flash_fwd_16(const T* __restrict__ Q, const T* __restrict__ K, const T* __restri
     // Per-head buffer resources: any offset past the head reads zero instead
     // of faulting (the tail below also clamps, so this is a safety net).
     const __amdgpu_buffer_rsrc_t krs =
-        __builtin_amdgcn_make_buffer_rsrc((void*)(K + kvbase), (short)0, n * ROWB, 0x00020000);
+        __builtin_amdgcn_make_buffer_rsrc((void*)(K + kvbase), (short)0, nk * ROWB, 0x00020000);
     const __amdgpu_buffer_rsrc_t vrs =
-        __builtin_amdgcn_make_buffer_rsrc((void*)(V + kvbase), (short)0, n * ROWB, 0x00020000);
+        __builtin_amdgcn_make_buffer_rsrc((void*)(V + kvbase), (short)0, nk * ROWB, 0x00020000);
 
     // DMA source offsets of this lane for the wave's units (within a tile).
     const int lrow = lane / CPR;             // row inside a unit
@@ -129,7 +133,7 @@ flash_fwd_16(const T* __restrict__ Q, const T* __restrict__ K, const T* __restri
         constexpr int st = decltype(stage)::value;
         char* kdst = (st ? ks1 : ks0) + wave * UPW * 1024;
         char* vdst = (st ? vs1 : vs0) + wave * UPW * 1024;
-        if (j0 + BC <= n) {
+        if (j0 + BC <= nk) {
 #pragma unroll
             for (int i = 0; i < UPW; ++i) {
                 dma16(krs, kdst + i * 1024, kvo[i], j0 * ROWB);
@@ -141,7 +145,7 @@ flash_fwd_16(const T* __restrict__ Q, const T* __restrict__ K, const T* __restri
 #pragma unroll
             for (int i = 0; i < UPW; ++i) {
                 const int r = (wave * UPW + i) * RPU + lrow;
-                const int g = min(j0 + r, n - 1) * ROWB;
+                const int g = min(j0 + r, nk - 1) * ROWB;
                 dma16(krs, kdst + i * 1024, g + 16 * (lch ^ swz_k<D>(r)), 0);
                 dma16(vrs, vdst + i * 1024, g + 16 * (lch ^ swz_v<D>(r)), 0);
             }
@@ -185,13 +189,13 @@ flash_fwd_16(const T* __restrict__ Q, const T* __restrict__ K, const T* __restri
             }
         }
 
-        const bool tail = j0 + BC > n;
+        const bool tail = j0 + BC > nk;
         if (tail) {
 #pragma unroll
             for (int kt = 0; kt < KT; ++kt)
 #pragma unroll
                 for (int r = 0; r < 16; ++r)
-                    if (j0 + 32 * kt + acc_row(r, half) >= n) s[kt][r] = -INFINITY;
+                    if (j0 + 32 * kt + acc_row(r, half) >= nk) s[kt][r] = -INFINITY;
         }
 
         float mt = -INFINITY;
@@ -219,7 +223,7 @@ flash_fwd_16(const T* __restrict__ Q, const T* __restrict__ K, const T* __restri
             for (int kt = 0; kt < KT; ++kt)
 #pragma unroll
                 for (int r = 0; r < 16; ++r)
-                    if (j0 + 32 * kt + acc_row(r, half) >= n) s[kt][r] = 0.f;
+                    if (j0 + 32 * kt + acc_row(r, half) >= nk) s[kt][r] = 0.f;
         }
 #pragma unroll
         for (int kt = 0; kt < KT; ++kt)
@@ -253,7 +257,7 @@ flash_fwd_16(const T* __restrict__ Q, const T* __restrict__ K, const T* __restri
     };
 
     // Two LDS stages: while one is computed on, the DMA fills the other.
-    const int ntiles = (n + BC - 1) / BC;
+    const int ntiles = (nk + BC - 1) / BC;
     issue_loads(0, Int<0>{});
     for (int t = 0;;) {
         __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0): this wave's DMA landed
@@ -271,17 +275,35 @@ flash_fwd_16(const T* __restrict__ Q, const T* __restrict__ K, const T* __restri
     const float ltot = pair_sum(lsum);
     if (qrow < n) {
         const float inv = 1.0f / ltot;
-        T* orow = O + base + (int64_t)qrow * D;
+        // Row hs n + qrow: the output row (one range: hs = bh), or the fp32
+        // partial row of key range hs % splits.
+        const int64_t orow0 = ((int64_t)hs * n + qrow) * D;
+        if constexpr (PART) {
+            float* orow = (float*)Out + orow0;
 #pragma unroll
-        for (int dt = 0; dt < DT; ++dt)
+            for (int dt = 0; dt < DT; ++dt)
 #pragma unroll
-            for (int g = 0; g < 4; ++g) {
-                float ov[4];
+                for (int g = 0; g < 4; ++g) {
+                    float4 ov;
+                    ov.x = acc[dt][4 * g + 0] * inv;
+                    ov.y = acc[dt][4 * g + 1] * inv;
+                    ov.z = acc[dt][4 * g + 2] * inv;
+                    ov.w = acc[dt][4 * g + 3] * inv;
+                    *(float4*)(orow + 32 * dt + 8 * g + 4 * half) = ov;
+                }
+        } else {
+            T* orow = (T*)Out + orow0;
 #pragma unroll
-                for (int e = 0; e < 4; ++e) ov[e] = acc[dt][4 * g + e] * inv;
-                *(u32x2*)(orow + 32 * dt + 8 * g + 4 * half) = M::pack4(ov);
-            }
-        if (half == 0) LSE[(int64_t)bh * n + qrow] = (mref + log2f(ltot)) * kLn2;
+            for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+                for (int g = 0; g < 4; ++g) {
+                    float ov[4];
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) ov[e] = acc[dt][4 * g + e] * inv;
+                    *(u32x2*)(orow + 32 * dt + 8 * g + 4 * half) = M::pack4(ov);
+                }
+        }
+        if (half == 0) LSE[(int64_t)hs * n + qrow] = (mref + log2f(ltot)) * kLn2;
     }
 }
 
@@ -302,11 +324,11 @@ flash_fwd_16(const T* __restrict__ Q, const T* __restrict__ K, const T* __restri
 // first reader.  The first K operands of the next MFMA phase are read into
 // registers at the end of each softmax phase.
 // ---------------------------------------------------------------------------
-template <typename T, int D>
+template <typename T, int D, bool PART>
 __global__ void __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2)))
 flash_fwd_pp(const T* __restrict__ Q, const T* __restrict__ K, const T* __restrict__ V,
-             T* __restrict__ O, float* __restrict__ LSE,
-             int n, int qtiles, int total, float c, int negate, int nh, int grp)
+             void* __restrict__ Out, float* __restrict__ LSE,
+             int n, int qtiles, int total, float c, int negate, int nh, int grp, int splits, int kchunk)
 {
     using M = Mfma<T>;
     constexpr int NW = 8;
@@ -338,12 +360,16 @@ flash_fwd_pp(const T* __restrict__ Q, const T* __restrict__ K, const T* __restri
     const int half = lane >> 5;
 
     const int tile = xcd_tile(blockIdx.x, total);
-    const int bh = tile / qtiles;
-    const int qt = tile - bh * qtiles;
+    const int hs = tile / qtiles;            // (b H + h) splits + key range
+    const int qt = tile - hs * qtiles;
+    const int bh = hs / splits;
+    const int kbeg = (hs - bh * splits) * kchunk;
+    const int nk = min(n - kbeg, kchunk);    // keys of this range (>= 1)
     const int64_t base = (int64_t)bh * n * D;
     // K/V head of this query head: query heads h of a batch share K/V head
-    // h / grp (grp = 1: one K/V head per query head).
-    const int64_t kvbase = (int64_t)((bh / nh) * (nh / grp) + (bh % nh) / grp) * n * D;
+    // h / grp (grp = 1: one K/V head per query head); the range starts at
+    // key kbeg.
+    const int64_t kvbase = (int64_t)((bh / nh) * (nh / grp) + (bh % nh) / grp) * n * D + (int64_t)kbeg * D;
     const int qrow = qt * BR + wave * 32 + col;
 
     // Q^T as the B operand: lane (col, half) holds Q[qrow][16 kc + 8 half + 0..7];
@@ -359,9 +385,9 @@ flash_fwd_pp(const T* __restrict__ Q, const T* __restrict__ K, const T* __restri
     }
 
     const __amdgpu_buffer_rsrc_t krs =
-        __builtin_amdgcn_make_buffer_rsrc((void*)(K + kvbase), (short)0, n * ROWB, 0x00020000);
+        __builtin_amdgcn_make_buffer_rsrc((void*)(K + kvbase), (short)0, nk * ROWB, 0x00020000);
     const __amdgpu_buffer_rsrc_t vrs =
-        __builtin_amdgcn_make_buffer_rsrc((void*)(V + kvbase), (short)0, n * ROWB, 0x00020000);
+        __builtin_amdgcn_make_buffer_rsrc((void*)(V + kvbase), (short)0, nk * ROWB, 0x00020000);
 
     // DMA: this wave moves units gw*UPW .. of a tile; K and V use their own
     // swizzles (chosen by the global chunk each lane fetches).
@@ -370,7 +396,7 @@ flash_fwd_pp(const T* __restrict__ Q, const T* __restrict__ K, const T* __restri
     auto issue = [&](__amdgpu_buffer_rsrc_t rs, char* stage, int j0, auto isk) {
         constexpr bool IK = decltype(isk)::value;
         char* dst = stage + gw * UPW * 1024;
-        if (j0 + BC <= n) {
+        if (j0 + BC <= nk) {
 #pragma unroll
             for (int i = 0; i < UPW; ++i) {
                 const int r = (gw * UPW + i) * RPU + lrow;
@@ -383,7 +409,7 @@ flash_fwd_pp(const T* __restrict__ Q, const T* __restrict__ K, const T* __restri
             for (int i = 0; i < UPW; ++i) {
                 const int r = (gw * UPW + i) * RPU + lrow;
                 const int sw = IK ? swz_k<D>(r) : swz_v<D>(r);
-                dma16(rs, dst + i * 1024, min(j0 + r, n - 1) * ROWB + 16 * (lch ^ sw), 0);
+                dma16(rs, dst + i * 1024, min(j0 + r, nk - 1) * ROWB + 16 * (lch ^ sw), 0);
             }
         }
     };
@@ -468,10 +494,10 @@ flash_fwd_pp(const T* __restrict__ Q, const T* __restrict__ K, const T* __restri
     // the end of a ragged last tile get score -inf, hence weight 0 (the host
     // never passes c = 0, so -inf * c stays -inf).
     auto softmax = [&](int j0) {
-        if (j0 + BC > n) {
+        if (j0 + BC > nk) {
 #pragma unroll
             for (int kt = 0; kt < KT; ++kt) {
-                const int lim = n - j0 - 32 * kt - 4 * half;
+                const int lim = nk - j0 - 32 * kt - 4 * half;
 #pragma unroll
                 for (int r = 0; r < 16; ++r)
                     if (8 * (r >> 2) + (r & 3) >= lim) s[kt][r] = -INFINITY;
@@ -527,7 +553,7 @@ flash_fwd_pp(const T* __restrict__ Q, const T* __restrict__ K, const T* __restri
         __builtin_amdgcn_sched_barrier(0);
     };
 
-    const int ntiles = (n + BC - 1) / BC;
+    const int ntiles = (nk + BC - 1) / BC;
     // Phase pair j (P = j & 1 selects the LDS stages at compile time):
     // MFMA phase j reads K_j from ks[P] and V_{j-1} from vs[1-P].
     auto pair = [&](int j, auto par, auto has_qk, auto has_pv, auto pf) {
@@ -584,17 +610,35 @@ flash_fwd_pp(const T* __restrict__ Q, const T* __restrict__ K, const T* __restri
     const float ltot = pair_sum(lsum);
     if (qrow < n) {
         const float inv = 1.0f / ltot;
-        T* orow = O + base + (int64_t)qrow * D;
+        // Row hs n + qrow: the output row (one range: hs = bh), or the fp32
+        // partial row of key range hs % splits.
+        const int64_t orow0 = ((int64_t)hs * n + qrow) * D;
+        if constexpr (PART) {
+            float* orow = (float*)Out + orow0;
 #pragma unroll
-        for (int dt = 0; dt < DT; ++dt)
+            for (int dt = 0; dt < DT; ++dt)
 #pragma unroll
-            for (int g = 0; g < 4; ++g) {
-                float ov[4];
+                for (int g = 0; g < 4; ++g) {
+                    float4 ov;
+                    ov.x = acc[dt][4 * g + 0] * inv;
+                    ov.y = acc[dt][4 * g + 1] * inv;
+                    ov.z = acc[dt][4 * g + 2] * inv;
+                    ov.w = acc[dt][4 * g + 3] * inv;
+                    *(float4*)(orow + 32 * dt + 8 * g + 4 * half) = ov;
+                }
+        } else {
+            T* orow = (T*)Out + orow0;
 #pragma unroll
-                for (int e = 0; e < 4; ++e) ov[e] = acc[dt][4 * g + e] * inv;
-                *(u32x2*)(orow + 32 * dt + 8 * g + 4 * half) = M::pack4(ov);
-            }
-        if (half == 0) LSE[(int64_t)bh * n + qrow] = (mref + log2f(ltot)) * kLn2;
+            for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+                for (int g = 0; g < 4; ++g) {
+                    float ov[4];
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) ov[e] = acc[dt][4 * g + e] * inv;
+                    *(u32x2*)(orow + 32 * dt + 8 * g + 4 * half) = M::pack4(ov);
+                }
+        }
+        if (half == 0) LSE[(int64_t)hs * n + qrow] = (mref + log2f(ltot)) * kLn2;
     }
 }
 
@@ -602,11 +646,11 @@ flash_fwd_pp(const T* __restrict__ Q, const T* __restrict__ K, const T* __restri
 // fp32 kernel: same structure on v_mfma_f32_32x32x2_f32 (one contraction
 // element per lane per instruction, so V needs no transpose in LDS).
 // ---------------------------------------------------------------------------
-template <int D, int BC, int NW>
+template <int D, int BC, int NW, bool PART>
 __global__ void __launch_bounds__(NW * 64)
 flash_fwd_32(const float* __restrict__ Q, const float* __restrict__ K, const float* __restrict__ V,
-             float* __restrict__ O, float* __restrict__ LSE,
-             int n, int qtiles, int total, float c, int negate, int nh, int grp)
+             void* __restrict__ Out, float* __restrict__ LSE,
+             int n, int qtiles, int total, float c, int negate, int nh, int grp, int splits, int kchunk)
 {
     constexpr int NT = NW * 64;
     constexpr int BR = 32 * NW;
@@ -626,12 +670,16 @@ flash_fwd_32(const float* __restrict__ Q, const float* __restrict__ K, const flo
     const int half = lane >> 5;
 
     const int tile = xcd_tile(blockIdx.x, total);
-    const int bh = tile / qtiles;
-    const int qt = tile - bh * qtiles;
+    const int hs = tile / qtiles;            // (b H + h) splits + key range
+    const int qt = tile - hs * qtiles;
+    const int bh = hs / splits;
+    const int kbeg = (hs - bh * splits) * kchunk;
+    const int nk = min(n - kbeg, kchunk);    // keys of this range (>= 1)
     const int64_t base = (int64_t)bh * n * D;
     // K/V head of this query head: query heads h of a batch share K/V head
-    // h / grp (grp = 1: one K/V head per query head).
-    const int64_t kvbase = (int64_t)((bh / nh) * (nh / grp) + (bh % nh) / grp) * n * D;
+    // h / grp (grp = 1: one K/V head per query head); the range starts at
+    // key kbeg.
+    const int64_t kvbase = (int64_t)((bh / nh) * (nh / grp) + (bh % nh) / grp) * n * D + (int64_t)kbeg * D;
     const float* __restrict__ Qh = Q + base;
     const float* __restrict__ Kh = K + kvbase;
     const float* __restrict__ Vh = V + kvbase;
@@ -657,7 +705,7 @@ flash_fwd_32(const float* __restrict__ Q, const float* __restrict__ K, const flo
         for (int i = 0; i < PER; ++i) {
             const int ch = tid + i * NT;
             const int key = ch / (D / 4), part = ch % (D / 4);
-            const bool ok = (CHUNKS % NT == 0 || ch < CHUNKS) && j0 + key < n;
+            const bool ok = (CHUNKS % NT == 0 || ch < CHUNKS) && j0 + key < nk;
             kreg[i] = ok ? *(const u32x4*)(Kh + (int64_t)(j0 + key) * D + 4 * part) : u32x4(0u);
             vreg[i] = ok ? *(const u32x4*)(Vh + (int64_t)(j0 + key) * D + 4 * part) : u32x4(0u);
         }
@@ -674,7 +722,7 @@ flash_fwd_32(const float* __restrict__ Q, const float* __restrict__ K, const flo
         }
     };
 
-    const int ntiles = (n + BC - 1) / BC;
+    const int ntiles = (nk + BC - 1) / BC;
     gload(0);
     for (int t = 0; t < ntiles; ++t) {
         const int j0 = t * BC;
@@ -693,13 +741,13 @@ flash_fwd_32(const float* __restrict__ Q, const float* __restrict__ K, const flo
                                                              qf[kc], s[kt], 0, 0, 0);
         }
 
-        const bool tail = j0 + BC > n;
+        const bool tail = j0 + BC > nk;
         if (tail) {
 #pragma unroll
             for (int kt = 0; kt < KT; ++kt)
 #pragma unroll
                 for (int r = 0; r < 16; ++r)
-                    if (j0 + 32 * kt + acc_row(r, half) >= n) s[kt][r] = -INFINITY;
+                    if (j0 + 32 * kt + acc_row(r, half) >= nk) s[kt][r] = -INFINITY;
         }
         float mt = -INFINITY;
 #pragma unroll
@@ -724,7 +772,7 @@ flash_fwd_32(const float* __restrict__ Q, const float* __restrict__ K, const flo
             for (int kt = 0; kt < KT; ++kt)
 #pragma unroll
                 for (int r = 0; r < 16; ++r)
-                    if (j0 + 32 * kt + acc_row(r, half) >= n) s[kt][r] = 0.f;
+                    if (j0 + 32 * kt + acc_row(r, half) >= nk) s[kt][r] = 0.f;
         }
 #pragma unroll
         for (int kt = 0; kt < KT; ++kt)
@@ -747,7 +795,9 @@ flash_fwd_32(const float* __restrict__ Q, const float* __restrict__ K, const flo
     const float ltot = pair_sum(lsum);
     if (qrow < n) {
         const float inv = 1.0f / ltot;
-        float* orow = O + base + (int64_t)qrow * D;
+        // Row hs n + qrow: the output row (one range: hs = bh), or the
+        // partial row of key range hs % splits (same type: fp32).
+        float* orow = (float*)Out + ((int64_t)hs * n + qrow) * D;
 #pragma unroll
         for (int dt = 0; dt < DT; ++dt)
 #pragma unroll
@@ -759,15 +809,16 @@ flash_fwd_32(const float* __restrict__ Q, const float* __restrict__ K, const flo
                 ov.w = acc[dt][4 * g + 3] * inv;
                 *(float4*)(orow + 32 * dt + 8 * g + 4 * half) = ov;
             }
-        if (half == 0) LSE[(int64_t)bh * n + qrow] = (mref + log2f(ltot)) * kLn2;
+        if (half == 0) LSE[(int64_t)hs * n + qrow] = (mref + log2f(ltot)) * kLn2;
     }
 }
 
 template <typename Kern, typename T>
-hipError_t launch(Kern kern, int nw, int br, const FwdArgs& a, hipStream_t stream) {
+hipError_t launch(Kern kern, int nw, int br, const FwdArgs& a, void* out, float* lse, int splits, int kchunk,
+                  hipStream_t stream) {
     const int n = (int)a.n;
     const int qtiles = (int)((a.n + br - 1) / br);
-    const int total = (int)(a.bh * qtiles);
+    const int total = (int)(a.bh * splits * qtiles);
     // c = |scale| log2(e) (a negative scale negates Q instead).  scale = 0 is
     // passed as the smallest normal float: every score times it is far below
     // the rounding of exp2 near 0, so the weights are exactly 1 as for c = 0,
@@ -777,42 +828,138 @@ hipError_t launch(Kern kern, int nw, int br, const FwdArgs& a, hipStream_t strea
     const T* q = (const T*)a.q;
     const T* k = (const T*)a.k;
     const T* v = (const T*)a.v;
-    T* o = (T*)a.o;
-    float* lse = a.lse;
     const int nh = (int)a.h, grp = (int)(a.h / a.hkv);
-    void* args[] = {&q, &k, &v, &o, &lse, (void*)&n, (void*)&qtiles, (void*)&total, (void*)&c, (void*)&negate,
-                    (void*)&nh, (void*)&grp};
+    void* args[] = {&q, &k, &v, &out, &lse, (void*)&n, (void*)&qtiles, (void*)&total, (void*)&c, (void*)&negate,
+                    (void*)&nh, (void*)&grp, (void*)&splits, (void*)&kchunk};
     return hipLaunchKernel((const void*)kern, dim3(total), dim3(nw * 64), args, 0, stream);
 }
 
-}  // namespace
-
-hipError_t launch_forward(const FwdArgs& a, hipStream_t stream) {
+// One launch of the kernel for (dtype, d); PART: fp32 partial outputs.
+template <bool PART>
+hipError_t launch_kernel(const FwdArgs& a, void* out, float* lse, int splits, int kchunk, hipStream_t stream) {
     constexpr int NW = 4;
     constexpr int BR = 32 * NW;
     switch (a.dtype) {
         case FA_DTYPE_BF16:
-            return a.d == 128 ? launch<decltype(&flash_fwd_pp<__bf16, 128>), __bf16>(
-                                    &flash_fwd_pp<__bf16, 128>, 8, 256, a, stream)
-                              : launch<decltype(&flash_fwd_16<__bf16, 64, 64, NW>), __bf16>(
-                                    &flash_fwd_16<__bf16, 64, 64, NW>, NW, BR, a, stream);
+            return a.d == 128 ? launch<decltype(&flash_fwd_pp<__bf16, 128, PART>), __bf16>(
+                                    &flash_fwd_pp<__bf16, 128, PART>, 8, 256, a, out, lse, splits, kchunk, stream)
+                              : launch<decltype(&flash_fwd_16<__bf16, 64, 64, NW, PART>), __bf16>(
+                                    &flash_fwd_16<__bf16, 64, 64, NW, PART>, NW, BR, a, out, lse, splits, kchunk,
+                                    stream);
         case FA_DTYPE_FP16:
-            return a.d == 128 ? launch<decltype(&flash_fwd_pp<_Float16, 128>), _Float16>(
-                                    &flash_fwd_pp<_Float16, 128>, 8, 256, a, stream)
-                              : launch<decltype(&flash_fwd_16<_Float16, 64, 64, NW>), _Float16>(
-                                    &flash_fwd_16<_Float16, 64, 64, NW>, NW, BR, a, stream);
+            return a.d == 128 ? launch<decltype(&flash_fwd_pp<_Float16, 128, PART>), _Float16>(
+                                    &flash_fwd_pp<_Float16, 128, PART>, 8, 256, a, out, lse, splits, kchunk, stream)
+                              : launch<decltype(&flash_fwd_16<_Float16, 64, 64, NW, PART>), _Float16>(
+                                    &flash_fwd_16<_Float16, 64, 64, NW, PART>, NW, BR, a, out, lse, splits, kchunk,
+                                    stream);
         case FA_DTYPE_FP32:
-            return a.d == 128 ? launch<decltype(&flash_fwd_32<128, 32, NW>), float>(
-                                    &flash_fwd_32<128, 32, NW>, NW, BR, a, stream)
-                              : launch<decltype(&flash_fwd_32<64, 64, NW>), float>(
-                                    &flash_fwd_32<64, 64, NW>, NW, BR, a, stream);
+            return a.d == 128 ? launch<decltype(&flash_fwd_32<128, 32, NW, PART>), float>(
+                                    &flash_fwd_32<128, 32, NW, PART>, NW, BR, a, out, lse, splits, kchunk, stream)
+                              : launch<decltype(&flash_fwd_32<64, 64, NW, PART>), float>(
+                                    &flash_fwd_32<64, 64, NW, PART>, NW, BR, a, out, lse, splits, kchunk, stream);
         default:
             return hipErrorInvalidValue;
     }
 }
 
+// ---------------------------------------------------------------------------
+// Merge of normalised partial results (the merge rule of the unite.ai page,
+// section "La Matemática detrás de la Atención Flash", formula 2, with its
+// normalisers restored, in log-sum-exp form): per row, with parts
+// (O_s, LSE_s), m = max_s LSE_s, w_s = exp(LSE_s - m):
+//     O = sum_s w_s O_s / sum_s w_s,   LSE = m + ln sum_s w_s.
+// A part with LSE_s = -inf weighs 0; a row whose parts are all -inf gets
+// O = 0, LSE = -inf.  D/4 lanes per row, 4 floats each; grid-stride.
+// ---------------------------------------------------------------------------
+template <typename T, int D>
+__global__ void __launch_bounds__(256)
+fa_merge_rows(const float* __restrict__ Op, const float* __restrict__ Lp, T* __restrict__ O,
+              float* __restrict__ LSE, int64_t G, int S, int64_t M)
+{
+    constexpr int LPR = D / 4;               // lanes per row
+    constexpr int RPB = 256 / LPR;           // rows per block pass
+    const int64_t rows = G * M;
+    const int part = threadIdx.x % LPR;
+    for (int64_t row = (int64_t)blockIdx.x * RPB + threadIdx.x / LPR; row < rows;
+         row += (int64_t)gridDim.x * RPB) {
+        const int64_t g = row / M;
+        const int64_t p0 = g * S * M + (row - g * M);   // part s of this row: p0 + s M
+        float m = -INFINITY;
+        for (int s = 0; s < S; ++s) m = fmaxf(m, Lp[p0 + s * M]);
+        const float ms = m == -INFINITY ? 0.f : m;
+        float l = 0.f;
+        float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+        for (int s = 0; s < S; ++s) {
+            const float w = __builtin_amdgcn_exp2f((Lp[p0 + s * M] - ms) * 1.4426950408889634f);
+            const float4 o = *(const float4*)(Op + (p0 + s * M) * D + 4 * part);
+            l += w;
+            acc.x = fmaf(w, o.x, acc.x);
+            acc.y = fmaf(w, o.y, acc.y);
+            acc.z = fmaf(w, o.z, acc.z);
+            acc.w = fmaf(w, o.w, acc.w);
+        }
+        const float inv = l > 0.f ? 1.0f / l : 0.f;
+        const float ov[4] = {acc.x * inv, acc.y * inv, acc.z * inv, acc.w * inv};
+        if constexpr (sizeof(T) == 4) {
+            *(float4*)((float*)O + row * D + 4 * part) = make_float4(ov[0], ov[1], ov[2], ov[3]);
+        } else {
+            *(u32x2*)(O + row * D + 4 * part) = Mfma<T>::pack4(ov);
+        }
+        if (part == 0) LSE[row] = l > 0.f ? m + logf(l) : -INFINITY;
+    }
+}
+
+template <typename T, int D>
+hipError_t launch_merge_t(const float* op, const float* lp, int64_t g, int64_t s, int64_t m, void* o, float* lse,
+                          hipStream_t stream) {
+    constexpr int RPB = 256 / (D / 4);
+    const int64_t need = (g * m + RPB - 1) / RPB;
+    const int blocks = (int)(need < 8192 ? need : 8192);
+    hipLaunchKernelGGL((fa_merge_rows<T, D>), dim3(blocks), dim3(256), 0, stream, op, lp, (T*)o, lse, g, (int)s, m);
+    return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_forward(const FwdArgs& a, hipStream_t stream) {
+    return launch_kernel<false>(a, a.o, a.lse, 1, (int)a.n, stream);
+}
+
+hipError_t launch_forward_split(const FwdArgs& a, int splits, int kchunk, float* o_part, float* lse_part,
+                                hipStream_t stream) {
+    hipError_t e = launch_kernel<true>(a, o_part, lse_part, splits, kchunk, stream);
+    if (e != hipSuccess) return e;
+    return launch_merge(o_part, lse_part, a.bh, splits, a.n, a.d, a.o, a.lse, a.dtype, stream);
+}
+
+hipError_t launch_merge(const float* o_parts, const float* lse_parts, int64_t g, int64_t s, int64_t m, int d,
+                        void* o, float* lse, int dtype, hipStream_t stream) {
+    switch (dtype) {
+        case FA_DTYPE_BF16:
+            return d == 128 ? launch_merge_t<__bf16, 128>(o_parts, lse_parts, g, s, m, o, lse, stream)
+                            : launch_merge_t<__bf16, 64>(o_parts, lse_parts, g, s, m, o, lse, stream);
+        case FA_DTYPE_FP16:
+            return d == 128 ? launch_merge_t<_Float16, 128>(o_parts, lse_parts, g, s, m, o, lse, stream)
+                            : launch_merge_t<_Float16, 64>(o_parts, lse_parts, g, s, m, o, lse, stream);
+        case FA_DTYPE_FP32:
+            return d == 128 ? launch_merge_t<float, 128>(o_parts, lse_parts, g, s, m, o, lse, stream)
+                            : launch_merge_t<float, 64>(o_parts, lse_parts, g, s, m, o, lse, stream);
+        default:
+            return hipErrorInvalidValue;
+    }
+}
+
+int forward_rows_per_workgroup(int dtype, int d) {
+    return (dtype != FA_DTYPE_FP32 && d == 128) ? 256 : 128;
+}
+
+int forward_workgroups_per_cu(int dtype, int d) {
+    return (dtype != FA_DTYPE_FP32 && d == 128) ? 1 : 2;
+}
+
 const char* kernel_config_string() {
     return "flash_fwd gfx950: d128 fp16/bf16 ping-pong 8 waves x 32 query rows, 64-key tiles; "
+           "key split into 64-key-aligned ranges + fp32 partial merge; "
            "d64 fp16/bf16 4 waves x 32 rows, 2 workgroups/CU; fp32 4 waves (key tile 64, d128: 32); "
            "MFMA 32x32x16 bf16/f16, 32x32x2 f32";
 }

@@ -39,6 +39,16 @@ def load_library():
         lib.fa_backward.argtypes = [ctypes.c_void_p] * 10 + [ctypes.c_int64] * 5 + [
             ctypes.c_float, ctypes.c_int, ctypes.c_void_p]
         lib.fa_backward.restype = ctypes.c_int
+        lib.fa_forward_split.argtypes = [ctypes.c_void_p] * 5 + [ctypes.c_int64] * 5 + [
+            ctypes.c_float, ctypes.c_int, ctypes.c_int64, ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p]
+        lib.fa_forward_split.restype = ctypes.c_int
+        lib.fa_split_workspace_bytes.argtypes = [ctypes.c_int64] * 5
+        lib.fa_split_workspace_bytes.restype = ctypes.c_int64
+        lib.fa_split_suggest.argtypes = [ctypes.c_int64] * 4 + [ctypes.c_int]
+        lib.fa_split_suggest.restype = ctypes.c_int64
+        lib.fa_merge.argtypes = [ctypes.c_void_p] * 2 + [ctypes.c_int64] * 4 + [
+            ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int, ctypes.c_void_p]
+        lib.fa_merge.restype = ctypes.c_int
         lib.fa_status_string.argtypes = [ctypes.c_int]
         lib.fa_status_string.restype = ctypes.c_char_p
         lib.fa_version.argtypes = []
@@ -57,6 +67,29 @@ def forward_into(q, k, v, o, lse, scale: float | None = None, stream=None) -> No
     q, o: (B, H, N, d); k, v: (B, H_kv, N, d) with H_kv dividing H (H_kv < H:
     grouped-query attention through fa_forward_gqa; H_kv = H: fa_forward)."""
     lib = load_library()
+    _check_forward(q, k, v, o, lse)
+    B, H, N, d = q.shape
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    handle = _stream_handle(q, stream)
+    with torch.cuda.device(q.device):
+        if k.shape[1] == H:
+            rc = lib.fa_forward(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(),
+                                B, H, N, d, float(scale), FA_DTYPE[q.dtype], handle)
+        else:
+            rc = lib.fa_forward_gqa(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(),
+                                    B, H, k.shape[1], N, d, float(scale), FA_DTYPE[q.dtype], handle)
+    if rc != 0:
+        raise RuntimeError(f"fa_forward failed: {status_string(rc)} ({rc})")
+
+
+def _stream_handle(t, stream):
+    if stream is None:
+        stream = torch.cuda.current_stream(t.device)
+    return stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
+
+
+def _check_forward(q, k, v, o, lse):
     for name, t in (("q", q), ("k", k), ("v", v), ("o", o), ("lse", lse)):
         if not t.is_cuda:
             raise ValueError(f"{name} must be a GPU tensor")
@@ -72,21 +105,87 @@ def forward_into(q, k, v, o, lse, scale: float | None = None, stream=None) -> No
         raise ValueError("k, v must be (B, H_kv, N, d) with H_kv dividing H")
     if tuple(lse.shape) != tuple(q.shape[:3]):
         raise ValueError("lse must have shape (B, H, N)")
+
+
+def split_suggest(B: int, H: int, N: int, d: int, dtype) -> int:
+    """The library's split count for these sizes (1: no split pays off)."""
+    return int(load_library().fa_split_suggest(B, H, N, d, FA_DTYPE[dtype]))
+
+
+def split_workspace_bytes(B: int, H: int, N: int, d: int, splits: int) -> int:
+    n = int(load_library().fa_split_workspace_bytes(B, H, N, d, splits))
+    if n < 0:
+        raise ValueError("invalid sizes for a key split")
+    return n
+
+
+def forward_split_into(q, k, v, o, lse, workspace, splits: int, scale: float | None = None, stream=None) -> None:
+    """forward_into with the keys cut into `splits` ranges merged afterwards;
+    workspace: a contiguous GPU tensor of at least split_workspace_bytes(...)
+    bytes (any dtype), which receives the fp32 partial results."""
+    lib = load_library()
+    _check_forward(q, k, v, o, lse)
+    if tuple(lse.shape) != tuple(q.shape[:3]):
+        raise ValueError("lse must have shape (B, H, N)")
+    if workspace is not None and (not workspace.is_cuda or not workspace.is_contiguous()):
+        raise ValueError("workspace must be a contiguous GPU tensor")
     B, H, N, d = q.shape
     if scale is None:
         scale = 1.0 / math.sqrt(d)
-    if stream is None:
-        stream = torch.cuda.current_stream(q.device)
-    handle = stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
+    ws_ptr = workspace.data_ptr() if workspace is not None else None
+    ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    handle = _stream_handle(q, stream)
     with torch.cuda.device(q.device):
-        if k.shape[1] == H:
-            rc = lib.fa_forward(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(),
-                                B, H, N, d, float(scale), FA_DTYPE[q.dtype], handle)
-        else:
-            rc = lib.fa_forward_gqa(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(),
-                                    B, H, k.shape[1], N, d, float(scale), FA_DTYPE[q.dtype], handle)
+        rc = lib.fa_forward_split(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(),
+                                  B, H, k.shape[1], N, d, float(scale), FA_DTYPE[q.dtype], int(splits),
+                                  ws_ptr, ws_bytes, handle)
     if rc != 0:
-        raise RuntimeError(f"fa_forward failed: {status_string(rc)} ({rc})")
+        raise RuntimeError(f"fa_forward_split failed: {status_string(rc)} ({rc})")
+
+
+def forward_split(q, k, v, splits: int | None = None, scale: float | None = None):
+    """(O, LSE) as forward(), computed over key ranges merged afterwards.
+    splits=None takes split_suggest(); the workspace comes from torch."""
+    B, H, N, d = q.shape
+    if splits is None:
+        splits = split_suggest(B, H, N, d, q.dtype)
+    o = torch.empty_like(q)
+    lse = torch.empty(q.shape[:3], dtype=torch.float32, device=q.device)
+    ws = torch.empty(max(split_workspace_bytes(B, H, N, d, splits), 16), dtype=torch.uint8, device=q.device)
+    forward_split_into(q, k, v, o, lse, ws, splits, scale)
+    return o, lse
+
+
+def merge_into(o_parts, lse_parts, o, lse, stream=None) -> None:
+    """Merge normalised partial results: o_parts (G, S, M, d) and lse_parts
+    (G, S, M) float32 into o (G, M, d) of o's dtype and lse (G, M)."""
+    lib = load_library()
+    for name, t in (("o_parts", o_parts), ("lse_parts", lse_parts), ("o", o), ("lse", lse)):
+        if not t.is_cuda or not t.is_contiguous():
+            raise ValueError(f"{name} must be a contiguous GPU tensor")
+    if o_parts.dtype != torch.float32 or lse_parts.dtype != torch.float32 or lse.dtype != torch.float32:
+        raise ValueError("o_parts, lse_parts and lse must be float32")
+    if o.dtype not in FA_DTYPE:
+        raise ValueError(f"o must be one of {list(FA_DTYPE)}")
+    if o_parts.dim() != 4 or tuple(lse_parts.shape) != tuple(o_parts.shape[:3]):
+        raise ValueError("o_parts must be (G, S, M, d) and lse_parts (G, S, M)")
+    G, S, M, d = o_parts.shape
+    if tuple(o.shape) != (G, M, d) or tuple(lse.shape) != (G, M):
+        raise ValueError("o must be (G, M, d) and lse (G, M)")
+    handle = _stream_handle(o, stream)
+    with torch.cuda.device(o.device):
+        rc = lib.fa_merge(o_parts.data_ptr(), lse_parts.data_ptr(), G, S, M, d, o.data_ptr(), lse.data_ptr(),
+                          FA_DTYPE[o.dtype], handle)
+    if rc != 0:
+        raise RuntimeError(f"fa_merge failed: {status_string(rc)} ({rc})")
+
+
+def merge(o_parts, lse_parts, dtype=torch.float32):
+    G, S, M, d = o_parts.shape
+    o = torch.empty((G, M, d), dtype=dtype, device=o_parts.device)
+    lse = torch.empty((G, M), dtype=torch.float32, device=o_parts.device)
+    merge_into(o_parts, lse_parts, o, lse)
+    return o, lse
 
 
 def forward(q, k, v, scale: float | None = None):

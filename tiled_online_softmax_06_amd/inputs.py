@@ -12,6 +12,7 @@ Recipe (one line per workload, same order as the workload table):
   gpt2     8 12   1024   64  bf16   N(0,1)              N(0,1)     1/sqrt(64)
   long     2 16   8192  128  bf16   N(0,1)              N(0,1)     1/sqrt(128)
   xlong    1  8  65536  128  bf16   N(0, sigma=3)       U(-1,1)    1/sqrt(128)
+  fewheads 1  2  16384  128  bf16   N(0,1)              N(0,1)     1/sqrt(128)
 
 Workload k (1-based, in the order above) uses ``numpy.random.default_rng(1000+k)``
 and draws Q, then K, then V as float32 arrays of shape (B, H, N, d); the
@@ -81,6 +82,9 @@ WORKLOADS = {
         Workload("long", 4, 2, 16, 8192, 128, "bf16"),
         Workload("xlong", 5, 1, 8, 65536, 128, "bf16", qk_sigma=3.0, v_dist="uniform",
                  sample_rows=256),
+        # few heads, long sequence: 128 query tiles of 256 rows leave half of
+        # 256 compute units idle unless the keys are split
+        Workload("fewheads", 6, 1, 2, 16384, 128, "bf16", sample_rows=256),
     )
 }
 
