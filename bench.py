@@ -18,6 +18,9 @@ dK), recomputation of S included, as is usual for attention backward.
 plus the merge kernel; workspace allocated before timing) with --splits
 ranges (0: the library's suggestion), counts 4*B*H*N^2*d like the forward,
 and also reports the unsplit forward on the same inputs.
+--op fp8 times one fa_forward_fp8 launch on the workload's draws quantised
+per tensor to OCP e4m3 (bf16 output), counts 4*B*H*N^2*d and takes the
+5000 TFLOP/s dense fp8 MFMA peak.
 --seq-len replaces the workload's N (same seeds and other sizes).
 """
 from __future__ import annotations
@@ -35,10 +38,12 @@ sys.path.insert(0, HERE)
 
 METRIC = "attention fwd TFLOP/s (4·B·H·N²·d) bf16 at 1 GPU + % of MFMA peak"
 METRIC_BWD = "attention bwd TFLOP/s (10·B·H·N²·d) at 1 GPU + % of MFMA peak"
+METRIC_FP8 = "attention fwd TFLOP/s (4·B·H·N²·d) fp8 e4m3 inputs at 1 GPU + % of fp8 MFMA peak"
 # MI355X published dense matrix peaks (TFLOP/s) and HBM bandwidth (GB/s).
-PEAK_TFLOPS = {"bf16": 2500.0, "fp16": 2500.0, "fp32": 157.3}
+PEAK_TFLOPS = {"bf16": 2500.0, "fp16": 2500.0, "fp32": 157.3, "fp8_e4m3": 5000.0}
 PEAK_HBM_GBS = 8000.0
 KERNEL_SOURCE = os.path.join(HERE, "tiled_online_softmax_06_amd", "csrc", "flash_fwd.hip")
+FP8_SOURCE = os.path.join(HERE, "tiled_online_softmax_06_amd", "csrc", "flash_fwd_fp8.hip")
 BWD_SOURCE = os.path.join(HERE, "tiled_online_softmax_06_amd", "csrc", "flash_bwd.hip")
 
 
@@ -161,7 +166,7 @@ def main():
                     help="K/V heads for a grouped-query run (0: one per query head)")
     ap.add_argument("--cpu-heads", type=int, default=0,
                     help="heads the CPU oracle computes in full (0: every head of the workload)")
-    ap.add_argument("--op", choices=("forward", "backward", "split"), default="forward")
+    ap.add_argument("--op", choices=("forward", "backward", "split", "fp8"), default="forward")
     ap.add_argument("--splits", type=int, default=0, help="key ranges for --op split (0: suggested)")
     ap.add_argument("--seq-len", type=int, default=0, help="override the workload's N (0: keep it)")
     ap.add_argument("--calibrate-copy", action="store_true",
@@ -201,6 +206,17 @@ def main():
 
     def step():
         fa.forward_into(qd, kd, vd, o, lse, w.scale, stream=stream)
+
+    fp8 = args.op == "fp8"
+    if fp8:
+        q8, k8, v8, descale = inputs.make_fp8_inputs(w, kv_heads=kv_heads)
+        q8d, k8d, v8d = (t.to(dev) for t in (q8, k8, v8))
+        o = torch.empty(q8.shape, dtype=torch.bfloat16, device=dev)
+        # the oracle (cpu_baseline) sees the dequantised values
+        q, k, v = (torch.from_numpy(inputs.dequantize(c, s_)) for c, s_ in zip((q8, k8, v8), descale))
+
+        def step():  # noqa: F811
+            fa.forward_fp8_into(q8d, k8d, v8d, descale, o, lse, w.scale, stream=stream)
 
     if backward:
         do = inputs.make_grad(w)
@@ -261,11 +277,13 @@ def main():
         flops = 10 * w.B * w.H * w.N * w.N * w.d
     tflops = flops / (ms * 1e-3) / 1e12
     props = torch.cuda.get_device_properties(dev)
-    peak = PEAK_TFLOPS[w.dtype]
+    peak = PEAK_TFLOPS["fp8_e4m3" if fp8 else w.dtype]
     roof = {"bound": "mfma", "achieved": round(tflops, 2), "peak": peak, "unit": "TFLOP/s",
             "frac": round(tflops / peak, 4), "traffic": None,
             "kernel": kernel_name(w),
             "avg_launch_ms": round(ms, 5)}
+    if fp8:
+        roof["kernel"] = f"flash_fwd_fp8<d={w.d}, bf16 out>"
     if split:
         roof["kernel"] = f"{kernel_name(w)} over {splits} key ranges + fa_merge_rows (one fa_forward_split call)"
         roof["avg_launch_ms_note"] = "the two kernels of one call, stream order"
@@ -273,13 +291,13 @@ def main():
         roof["kernel"] = (f"flash_bwd_dot + flash_bwd_dq + flash_bwd_dkdv <{w.dtype}, d={w.d}> "
                           "(one fa_backward call)")
         roof["avg_launch_ms_note"] = "the three kernels of one call, stream order"
-    rec = None if backward or split or args.seq_len else traffic_record(w.name)
+    rec = None if backward or split or fp8 or args.seq_len else traffic_record(w.name)
     if rec is not None:
         roof["traffic"] = rec["hbm_bytes_per_launch"]
         roof["traffic_note"] = rec.get("note", "")
 
     result = {
-        "metric": METRIC if not backward else METRIC_BWD,
+        "metric": METRIC_BWD if backward else (METRIC_FP8 if fp8 else METRIC),
         "value": round(tflops, 2),
         "unit": "TFLOP/s",
         "n_gpus": 1,
@@ -289,7 +307,7 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": w.dtype,
+        "dtype": "fp8_e4m3" if fp8 else w.dtype,
         "data": "synthetic (seeded iid normal inputs, see tiled_online_softmax_06_amd/inputs.py)",
         "config": {"workload": f"{w.name}: B={w.B} H={w.H} N={w.N} d={w.d} {w.dtype}, non-causal, "
                                f"scale=1/sqrt({w.d})" + (f", {kv_heads} K/V heads" if kv_heads != w.H else ""),
@@ -298,18 +316,22 @@ def main():
         "roofline": roof,
         "device": {"name": props.name, "cu": props.multi_processor_count,
                    "gcn_arch": getattr(props, "gcnArchName", "")},
-        "kernel_sha256_16": kernel_hash(BWD_SOURCE if backward else KERNEL_SOURCE),
+        "kernel_sha256_16": kernel_hash(BWD_SOURCE if backward else (FP8_SOURCE if fp8 else KERNEL_SOURCE)),
     }
     if backward:
         result["op"] = "backward"
         result["config"]["op"] = "backward"
+    if fp8:
+        result["op"] = "fp8"
+        result["config"]["op"] = "fp8"
+        result["config"]["descale"] = [round(x, 8) for x in descale]
     if split:
         result["op"] = "split"
         result["config"]["op"] = "split"
         result["config"]["splits"] = splits
         result["unsplit"] = {"ms_per_step": round(unsplit_ms, 5),
                              "value": round(flops / (unsplit_ms * 1e-3) / 1e12, 2)}
-    if not args.no_cpu_baseline and split:
+    if not args.no_cpu_baseline and (split or fp8):
         workers = max(1, min(16, len(os.sched_getaffinity(0))))
         result["cpu_baseline"] = cpu_baseline(w, q, k, v, args.cpu_heads, 512, workers,
                                               gpu_out=(o.cpu(), lse.cpu()))

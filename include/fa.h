@@ -146,6 +146,32 @@ int fa_backward(const void* Q, const void* K, const void* V, const void* O, cons
                 float scale, int dtype, hipStream_t stream);
 
 /*
+ * fa_forward_fp8 — the forward pass with FP8 inputs.  The unite.ai page,
+ * section "Atención Flash-3", names low-precision FP8 for the attention
+ * products without fixing a format or scaling; this is the reading:
+ *
+ * Q, K, V  device, read only: OCP FP8 E4M3 codes (1 byte each: sign, 4
+ *          exponent bits with bias 7, 3 mantissa bits; no infinities, S.1111.111
+ *          is NaN), layouts as for fa_forward_gqa ((B, H, N, d) and
+ *          (B, H_kv, N, d)).  The values they stand for are
+ *          q_descale * Q, k_descale * K, v_descale * V (float32 factors,
+ *          one per tensor, any finite value).
+ * O        device, written: (B, H, N, d) of out_dtype (FA_DTYPE_BF16,
+ *          FA_DTYPE_FP16 or FA_DTYPE_FP32), the attention output of the
+ *          dequantised values, rounded to nearest even.
+ * LSE      device, written: (B, H, N) float32,
+ *          ln sum_j exp(scale * q_descale * k_descale * <Q_i, K_j>).
+ * Both products run on the e4m3 matrix instructions (float32 accumulation);
+ * the softmax is float32; the weights P are rounded to e4m3 before the
+ * product with V.  Everything else (shapes, d, H_kv, ownership, errors) as
+ * for fa_forward_gqa; a non-finite descale factor is FA_ERR_BAD_SCALE.
+ */
+int fa_forward_fp8(const void* Q, const void* K, const void* V, void* O, float* LSE,
+                   int64_t B, int64_t H, int64_t H_kv, int64_t N, int64_t d,
+                   float scale, float q_descale, float k_descale, float v_descale,
+                   int out_dtype, hipStream_t stream);
+
+/*
  * fa_forward_split — fa_forward_gqa with the keys of every head cut into
  * ranges processed by separate workgroups, then merged.  For few heads and
  * long sequences (B*H*ceil(N/256) below the number of compute units) this

@@ -36,7 +36,7 @@ def _header_enum(name):
 
 def test_exports_every_declared_function(lib):
     funcs = _header_functions()
-    assert set(funcs) == {"fa_forward", "fa_forward_gqa", "fa_backward", "fa_forward_split",
+    assert set(funcs) == {"fa_forward", "fa_forward_gqa", "fa_backward", "fa_forward_split", "fa_forward_fp8",
                           "fa_split_workspace_bytes", "fa_split_suggest", "fa_merge", "fa_status_string",
                           "fa_version"}
     out = subprocess.run(["nm", "-D", "--defined-only", lib._name], capture_output=True, text=True).stdout
@@ -248,3 +248,29 @@ def test_merge_error_codes(lib):
     assert call_merge(lib, lse=A + 512 * MB + 64) == codes["FA_ERR_ALIAS"]      # LSE inside O
     assert call_merge(lib, lse=A + 256 * MB) == codes["FA_ERR_ALIAS"]           # LSE on the LSE parts
     assert call_merge(lib, M=0, op=None, lp=None, o=None, lse=None) == 0
+
+
+def call_fp8(lib, q=A, k=A + 64 * MB, v=A + 128 * MB, o=A + 192 * MB, lse=A + 256 * MB, B=1, H=2, Hkv=2, N=1000,
+             d=128, scale=0.1, dq=0.01, dk=0.01, dv=0.01, out=2):
+    lib.fa_forward_fp8.argtypes = [ctypes.c_void_p] * 5 + [ctypes.c_int64] * 5 + [ctypes.c_float] * 4 + [
+        ctypes.c_int, ctypes.c_void_p]
+    return lib.fa_forward_fp8(q, k, v, o, lse, B, H, Hkv, N, d, scale, dq, dk, dv, out, None)
+
+
+def test_fp8_error_codes(lib):
+    codes = _header_enum("fa_status_t")
+    assert call_fp8(lib, N=-1) == codes["FA_ERR_BAD_SHAPE"]
+    assert call_fp8(lib, Hkv=3) == codes["FA_ERR_BAD_SHAPE"]
+    assert call_fp8(lib, N=1 << 25) == codes["FA_ERR_BAD_SHAPE"]              # 4 GiB per head > 32-bit offsets
+    assert call_fp8(lib, out=7) == codes["FA_ERR_UNSUPPORTED_DTYPE"]
+    assert call_fp8(lib, d=256) == codes["FA_ERR_UNSUPPORTED_HEAD_DIM"]
+    for field in ("scale", "dq", "dk", "dv"):
+        assert call_fp8(lib, **{field: math.inf}) == codes["FA_ERR_BAD_SCALE"], field
+        assert call_fp8(lib, **{field: math.nan}) == codes["FA_ERR_BAD_SCALE"], field
+    for field in ("q", "k", "v", "o", "lse"):
+        assert call_fp8(lib, **{field: None}) == codes["FA_ERR_NULL_POINTER"], field
+    assert call_fp8(lib, k=A + 64 * MB + 8) == codes["FA_ERR_MISALIGNED"]
+    # O (bf16, 512,000 B) runs into LSE; Q is 256,000 B of codes
+    assert call_fp8(lib, lse=A + 192 * MB + 511_000) == codes["FA_ERR_ALIAS"]
+    assert call_fp8(lib, o=A + 255_984) == codes["FA_ERR_ALIAS"]
+    assert call_fp8(lib, N=0, q=None, k=None, v=None, o=None, lse=None) == 0

@@ -9,6 +9,8 @@ from .fa import (  # noqa: F401
     backward,
     backward_into,
     forward,
+    forward_fp8,
+    forward_fp8_into,
     forward_into,
     forward_split,
     forward_split_into,

@@ -15,7 +15,7 @@ import sys
 
 HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
-SOURCES = [os.path.join(HERE, "csrc", f) for f in ("flash_fwd.hip", "flash_bwd.hip", "fa_api.hip")]
+SOURCES = [os.path.join(HERE, "csrc", f) for f in ("flash_fwd.hip", "flash_fwd_fp8.hip", "flash_bwd.hip", "fa_api.hip")]
 OUTPUT = os.path.join(HERE, "libfa.so")
 ARCH = "gfx950"
 FLAGS = [

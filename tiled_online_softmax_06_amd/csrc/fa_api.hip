@@ -100,6 +100,38 @@ extern "C" int fa_forward(const void* Q, const void* K, const void* V, void* O, 
     return fa_forward_gqa(Q, K, V, O, LSE, B, H, H, N, d, scale, dtype, stream);
 }
 
+extern "C" int fa_forward_fp8(const void* Q, const void* K, const void* V, void* O, float* LSE,
+                              int64_t B, int64_t H, int64_t Hkv, int64_t N, int64_t d,
+                              float scale, float q_descale, float k_descale, float v_descale,
+                              int out_dtype, hipStream_t stream) {
+    if (B < 0 || H < 0 || N < 0 || d < 0 || Hkv < 0) return FA_ERR_BAD_SHAPE;
+    if (out_dtype != FA_DTYPE_FP32 && out_dtype != FA_DTYPE_FP16 && out_dtype != FA_DTYPE_BF16)
+        return FA_ERR_UNSUPPORTED_DTYPE;
+    if (d != 64 && d != 128) return FA_ERR_UNSUPPORTED_HEAD_DIM;
+    if (!isfinite(scale) || !isfinite(q_descale) || !isfinite(k_descale) || !isfinite(v_descale))
+        return FA_ERR_BAD_SCALE;
+    const int64_t oesize = out_dtype == FA_DTYPE_FP32 ? 4 : 2;
+    int64_t bh = 0, rows = 0, bytes = 0, obytes = 0, bkv = 0, kvrows = 0, kvbytes = 0;
+    if (!mul_ok(B, H, &bh) || !mul_ok(bh, N, &rows) || !mul_ok(rows, d, &bytes) || !mul_ok(bytes, oesize, &obytes) ||
+        !mul_ok(B, Hkv, &bkv) || !mul_ok(bkv, N, &kvrows) || !mul_ok(kvrows, d, &kvbytes))
+        return FA_ERR_BAD_SHAPE;
+    if (rows == 0) return FA_OK;
+    if (Hkv == 0 || H % Hkv != 0) return FA_ERR_BAD_SHAPE;
+    if (N > INT32_MAX || H > INT32_MAX || N * d > INT32_MAX) return FA_ERR_BAD_SHAPE;
+    const int64_t tiles = bh * ((N + fa::kMinRowsPerWorkgroup - 1) / fa::kMinRowsPerWorkgroup);
+    if (tiles > INT32_MAX) return FA_ERR_BAD_SHAPE;
+    if (!Q || !K || !V || !O || !LSE) return FA_ERR_NULL_POINTER;
+    if (((uintptr_t)Q | (uintptr_t)K | (uintptr_t)V | (uintptr_t)O) & 15u) return FA_ERR_MISALIGNED;
+    if ((uintptr_t)LSE & 3u) return FA_ERR_MISALIGNED;
+    const int64_t lbytes = rows * 4;
+    if (overlaps(O, obytes, Q, bytes) || overlaps(O, obytes, K, kvbytes) || overlaps(O, obytes, V, kvbytes) ||
+        overlaps(LSE, lbytes, Q, bytes) || overlaps(LSE, lbytes, K, kvbytes) ||
+        overlaps(LSE, lbytes, V, kvbytes) || overlaps(LSE, lbytes, O, obytes))
+        return FA_ERR_ALIAS;
+    fa::Fp8Args a{Q, K, V, O, LSE, bh, H, Hkv, N, (int)d, out_dtype, scale, q_descale, k_descale, v_descale};
+    return fa::launch_forward_fp8(a, stream) == hipSuccess ? FA_OK : FA_ERR_LAUNCH;
+}
+
 extern "C" int64_t fa_split_workspace_bytes(int64_t B, int64_t H, int64_t N, int64_t d, int64_t splits) {
     if (B < 0 || H < 0 || N < 0 || d < 1 || splits < 1) return -1;
     int64_t bh = 0, ranges = 0, kchunk = 0, ob = 0, lb = 0;

@@ -1,5 +1,5 @@
 // Internal interface between the C-ABI layer (fa_api.hip) and the kernels
-// (flash_fwd.hip, flash_bwd.hip).  Not installed; include/fa.h is the public header.
+// (flash_fwd.hip, flash_fwd_fp8.hip, flash_bwd.hip).  Not installed; include/fa.h is the public header.
 #pragma once
 
 #include <stdint.h>
@@ -41,6 +41,25 @@ struct BwdArgs {
     int dtype;       // fp16 or bf16
     float scale;
 };
+
+struct Fp8Args {
+    const void* q;   // e4m3 codes, (B, H, N, d)
+    const void* k;   // e4m3 codes, (B, Hkv, N, d)
+    const void* v;
+    void* o;         // (B, H, N, d) of out_dtype
+    float* lse;
+    int64_t bh;
+    int64_t h;
+    int64_t hkv;
+    int64_t n;
+    int d;
+    int out_dtype;   // fa_dtype_t of O
+    float scale;
+    float q_descale, k_descale, v_descale;
+};
+
+// Launches the FP8 forward kernel on `stream` (checked arguments).
+hipError_t launch_forward_fp8(const Fp8Args& a, hipStream_t stream);
 
 // Launches the backward kernels (row dots, dQ, dK/dV) on `stream`.
 hipError_t launch_backward(const BwdArgs& a, hipStream_t stream);

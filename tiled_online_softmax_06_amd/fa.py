@@ -49,6 +49,9 @@ def load_library():
         lib.fa_merge.argtypes = [ctypes.c_void_p] * 2 + [ctypes.c_int64] * 4 + [
             ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int, ctypes.c_void_p]
         lib.fa_merge.restype = ctypes.c_int
+        lib.fa_forward_fp8.argtypes = [ctypes.c_void_p] * 5 + [ctypes.c_int64] * 5 + [ctypes.c_float] * 4 + [
+            ctypes.c_int, ctypes.c_void_p]
+        lib.fa_forward_fp8.restype = ctypes.c_int
         lib.fa_status_string.argtypes = [ctypes.c_int]
         lib.fa_status_string.restype = ctypes.c_char_p
         lib.fa_version.argtypes = []
@@ -185,6 +188,48 @@ def merge(o_parts, lse_parts, dtype=torch.float32):
     o = torch.empty((G, M, d), dtype=dtype, device=o_parts.device)
     lse = torch.empty((G, M), dtype=torch.float32, device=o_parts.device)
     merge_into(o_parts, lse_parts, o, lse)
+    return o, lse
+
+
+FP8_DTYPES = (torch.float8_e4m3fn, torch.uint8)
+
+
+def forward_fp8_into(q8, k8, v8, descale, o, lse, scale: float | None = None, stream=None) -> None:
+    """FP8 forward: q8, k8, v8 hold OCP e4m3 codes (torch.float8_e4m3fn or
+    raw uint8), descale = (q_descale, k_descale, v_descale) the per-tensor
+    factors of their values; o (B, H, N, d) in bf16 / fp16 / fp32 and lse
+    (B, H, N) float32 are written."""
+    lib = load_library()
+    for name, t in (("q8", q8), ("k8", k8), ("v8", v8), ("o", o), ("lse", lse)):
+        if not t.is_cuda or not t.is_contiguous():
+            raise ValueError(f"{name} must be a contiguous GPU tensor")
+    if q8.dtype not in FP8_DTYPES or k8.dtype not in FP8_DTYPES or v8.dtype not in FP8_DTYPES:
+        raise ValueError("q8, k8, v8 must be float8_e4m3fn (or uint8 codes)")
+    if o.dtype not in FA_DTYPE or lse.dtype != torch.float32:
+        raise ValueError("o must be float32 / float16 / bfloat16 and lse float32")
+    if q8.dim() != 4 or o.shape != q8.shape or k8.dim() != 4 or v8.shape != k8.shape:
+        raise ValueError("q8, o must be (B, H, N, d) and k8, v8 one shape (B, H_kv, N, d)")
+    if k8.shape[0] != q8.shape[0] or k8.shape[2:] != q8.shape[2:] or k8.shape[1] < 1 or q8.shape[1] % k8.shape[1]:
+        raise ValueError("k8, v8 must be (B, H_kv, N, d) with H_kv dividing H")
+    if tuple(lse.shape) != tuple(q8.shape[:3]):
+        raise ValueError("lse must have shape (B, H, N)")
+    B, H, N, d = q8.shape
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    dq, dk, dv = (float(x) for x in descale)
+    handle = _stream_handle(q8, stream)
+    with torch.cuda.device(q8.device):
+        rc = lib.fa_forward_fp8(q8.data_ptr(), k8.data_ptr(), v8.data_ptr(), o.data_ptr(), lse.data_ptr(),
+                                B, H, k8.shape[1], N, d, float(scale), dq, dk, dv, FA_DTYPE[o.dtype], handle)
+    if rc != 0:
+        raise RuntimeError(f"fa_forward_fp8 failed: {status_string(rc)} ({rc})")
+
+
+def forward_fp8(q8, k8, v8, descale, scale: float | None = None, out_dtype=torch.bfloat16):
+    """Returns (O, LSE) of the FP8 forward; O in out_dtype."""
+    o = torch.empty(q8.shape, dtype=out_dtype, device=q8.device)
+    lse = torch.empty(q8.shape[:3], dtype=torch.float32, device=q8.device)
+    forward_fp8_into(q8, k8, v8, descale, o, lse, scale)
     return o, lse
 
 

@@ -22,6 +22,11 @@ upcast exactly to float64, to the oracle.  The "xlong" workload is checked on
 256 distinct flat (b, h, n) query indices drawn without replacement by
 ``default_rng(2005)`` and sorted.
 
+FP8 inputs: the workload's float32 draws (before any rounding) are quantised
+per tensor to OCP e4m3: descale = max|x| / 448 (float32), codes =
+round-to-nearest-even(x / descale) (torch's ``Tensor.to(float8_e4m3fn)``);
+the values are codes * descale, upcast exactly to float64 for the oracle.
+
 Backward pass: the upstream gradient dO of workload k is N(0, 1) of shape
 (B, H, N, d) from ``default_rng(3000+k)``, rounded to the storage dtype the
 same way; ``random_grad`` draws one for any shape and seed.
@@ -123,6 +128,49 @@ def random_qkv(shape, dtype: str, seed: int, sigma: float = 1.0, kv_heads: int |
             x *= np.float32(sigma)
         out.append(torch.from_numpy(x).to(DTYPES[dtype]).contiguous())
     return tuple(out)
+
+
+def quantize_e4m3(x: np.ndarray):
+    """Per-tensor e4m3 quantisation: (codes as torch.float8_e4m3fn, descale)."""
+    x = np.asarray(x, dtype=np.float32)
+    amax = float(np.abs(x).max()) if x.size else 0.0
+    descale = np.float32(amax / 448.0) if amax > 0 else np.float32(1.0)
+    codes = torch.from_numpy(x / descale).to(torch.float8_e4m3fn).contiguous()
+    return codes, float(descale)
+
+
+def make_fp8_inputs(w: Workload, seed: int | None = None, kv_heads: int | None = None):
+    """(q8, k8, v8, (dq, dk, dv)): the workload's float32 draws quantised to
+    e4m3 per tensor (the workload's own dtype is ignored)."""
+    rng = np.random.default_rng(w.seed if seed is None else seed)
+    shape = (w.B, w.H, w.N, w.d)
+    kv_shape = (w.B, w.H if kv_heads is None else kv_heads, w.N, w.d)
+    q = rng.standard_normal(shape, dtype=np.float32) * np.float32(w.qk_sigma)
+    k = rng.standard_normal(kv_shape, dtype=np.float32) * np.float32(w.qk_sigma)
+    if w.v_dist == "uniform":
+        v = rng.uniform(-1.0, 1.0, size=kv_shape).astype(np.float32)
+    else:
+        v = rng.standard_normal(kv_shape, dtype=np.float32)
+    (q8, dq), (k8, dk), (v8, dv) = (quantize_e4m3(x) for x in (q, k, v))
+    return q8, k8, v8, (dq, dk, dv)
+
+
+def random_fp8(shape, seed: int, sigma: float = 1.0, kv_heads: int | None = None):
+    """Generic seeded e4m3 (q8, k8, v8, descales) from N(0, sigma) draws."""
+    rng = np.random.default_rng(seed)
+    kv_shape = tuple(shape) if kv_heads is None else (shape[0], kv_heads) + tuple(shape[2:])
+    out, ds = [], []
+    for i in range(3):
+        x = rng.standard_normal(shape if i == 0 else kv_shape, dtype=np.float32) * np.float32(sigma)
+        c, s = quantize_e4m3(x)
+        out.append(c)
+        ds.append(s)
+    return out[0], out[1], out[2], tuple(ds)
+
+
+def dequantize(codes: torch.Tensor, descale: float) -> np.ndarray:
+    """Exact float64 values of e4m3 codes times their float32 descale."""
+    return codes.cpu().to(torch.float64).numpy() * float(np.float32(descale))
 
 
 def make_grad(w: Workload, seed: int | None = None):
