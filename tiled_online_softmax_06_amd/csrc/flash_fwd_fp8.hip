@@ -84,16 +84,15 @@ template <> struct Store4<float> {
     }
 };
 
-// Workgroup: 4 waves x 32 query rows of one (b, h); K/V tiles of 64 keys
-// DMA'd into double-buffered LDS; two workgroups per CU.
-template <int D, typename OutT>
+// Workgroup: 4 waves x 32 query rows of one (b, h); K/V tiles of BC keys
+// (a multiple of 64) DMA'd into double-buffered LDS; two workgroups per CU.
+template <int D, int BC, typename OutT>
 __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2)))
 flash_fwd_fp8(const uint8_t* __restrict__ Q, const uint8_t* __restrict__ K, const uint8_t* __restrict__ V,
               OutT* __restrict__ O, float* __restrict__ LSE,
               int n, int qtiles, int total, float c, int negate, float vscale, int nh, int grp)
 {
     constexpr int NW = 4;
-    constexpr int BC = 64;                   // keys per tile
     constexpr int BR = 32 * NW;              // query rows per workgroup
     constexpr int ROWB = D;                  // bytes per K/V row
     constexpr int CPR = D / 16;              // 16-byte chunks per row
@@ -104,7 +103,8 @@ flash_fwd_fp8(const uint8_t* __restrict__ Q, const uint8_t* __restrict__ K, cons
     constexpr int KT = BC / 32;              // 32-key sub-tiles
     constexpr int DT = D / 32;               // 32-wide output column blocks
     constexpr int KC = D / 64;               // 64-dim contraction chunks of Q.K^T
-    static_assert(UNITS % NW == 0 && KT == 2, "tile shape");
+    constexpr int G = BC / 64;               // 64-key groups (one P.V MFMA each)
+    static_assert(UNITS % NW == 0 && BC % 64 == 0, "tile shape");
 
     __shared__ __attribute__((aligned(1024))) char ks0[TILEB];
     __shared__ __attribute__((aligned(1024))) char vs0[TILEB];
@@ -252,8 +252,9 @@ flash_fwd_fp8(const uint8_t* __restrict__ Q, const uint8_t* __restrict__ K, cons
         // P^T as the B operand: dword (kt, q) holds keys 32 kt + 8 q + 4 half
         // + 0..3; swapping the upper half of dword 2p with the lower half of
         // dword 2p + 1 leaves lane half h with keys 32 kt + 16 p + 8 h + 0..7
-        // in (dword 2p, dword 2p + 1), i.e. read r = 2 kt + p.
-        int pw[8];
+        // in (dword 2p, dword 2p + 1), i.e. read r = 2 kt + p of 64-key
+        // group kt / 2.
+        int pw[8 * G];
 #pragma unroll
         for (int kt = 0; kt < KT; ++kt)
 #pragma unroll
@@ -264,17 +265,22 @@ flash_fwd_fp8(const uint8_t* __restrict__ Q, const uint8_t* __restrict__ K, cons
                 pw[4 * kt + 2 * p + 0] = (int)sw[0];
                 pw[4 * kt + 2 * p + 1] = (int)sw[1];
             }
-        const i32x8 bp = {pw[0], pw[1], pw[2], pw[3], pw[4], pw[5], pw[6], pw[7]};
-
-        // O^T += V^T P^T: four transpose reads of 8 keys per operand.
+        // O^T += V^T P^T: per 64-key group, four transpose reads of 8 keys
+        // per operand.
 #pragma unroll
-        for (int dt = 0; dt < DT; ++dt) {
-            i32x2 r4[4];
+        for (int g = 0; g < G; ++g) {
+            const int* w = pw + 8 * g;
+            const i32x8 bp = {w[0], w[1], w[2], w[3], w[4], w[5], w[6], w[7]};
 #pragma unroll
-            for (int r = 0; r < 4; ++r)
-                r4[r] = __builtin_amdgcn_ds_read_tr8_b64_v2i32((lds_i32x2)(vb + 16 * r * ROWB + voff[dt]));
-            const i32x8 a = {r4[0].x, r4[0].y, r4[1].x, r4[1].y, r4[2].x, r4[2].y, r4[3].x, r4[3].y};
-            acc[dt] = mfma_fp8(a, bp, acc[dt]);
+            for (int dt = 0; dt < DT; ++dt) {
+                i32x2 r4[4];
+#pragma unroll
+                for (int r = 0; r < 4; ++r)
+                    r4[r] = __builtin_amdgcn_ds_read_tr8_b64_v2i32(
+                        (lds_i32x2)(vb + (64 * g + 16 * r) * ROWB + voff[dt]));
+                const i32x8 a = {r4[0].x, r4[0].y, r4[1].x, r4[1].y, r4[2].x, r4[2].y, r4[3].x, r4[3].y};
+                acc[dt] = mfma_fp8(a, bp, acc[dt]);
+            }
         }
     };
 
@@ -310,7 +316,7 @@ flash_fwd_fp8(const uint8_t* __restrict__ Q, const uint8_t* __restrict__ K, cons
     }
 }
 
-template <int D, typename OutT>
+template <int D, int BC, typename OutT>
 hipError_t launch_fp8_t(const Fp8Args& a, hipStream_t stream) {
     constexpr int BR = 128;
     const int n = (int)a.n;
@@ -331,12 +337,12 @@ hipError_t launch_fp8_t(const Fp8Args& a, hipStream_t stream) {
     const int nh = (int)a.h, grp = (int)(a.h / a.hkv);
     void* args[] = {&q, &k, &v, &o, &lse, (void*)&n, (void*)&qtiles, (void*)&total, (void*)&c, (void*)&negate,
                     (void*)&vscale, (void*)&nh, (void*)&grp};
-    return hipLaunchKernel((const void*)&flash_fwd_fp8<D, OutT>, dim3(total), dim3(256), args, 0, stream);
+    return hipLaunchKernel((const void*)&flash_fwd_fp8<D, BC, OutT>, dim3(total), dim3(256), args, 0, stream);
 }
 
 template <typename OutT>
 hipError_t launch_fp8_out(const Fp8Args& a, hipStream_t stream) {
-    return a.d == 128 ? launch_fp8_t<128, OutT>(a, stream) : launch_fp8_t<64, OutT>(a, stream);
+    return a.d == 128 ? launch_fp8_t<128, 64, OutT>(a, stream) : launch_fp8_t<64, 64, OutT>(a, stream);
 }
 
 }  // namespace
