@@ -200,8 +200,10 @@ def test_split_suggest(lib):
     assert lib.fa_split_suggest(2, 16, 8192, 128, 2) == 1       # 1024 workgroups already
     assert lib.fa_split_suggest(1, 2, 16384, 128, 2) == 2       # 128 workgroups -> 256
     assert lib.fa_split_suggest(1, 1, 8192, 128, 2) == 8        # 32 -> 256, 1024 keys per range
-    assert lib.fa_split_suggest(1, 1, 1024, 128, 2) == 2        # capped at 512 keys per range
+    assert lib.fa_split_suggest(1, 1, 1024, 128, 2) == 1        # tiny: a second launch costs more
     assert lib.fa_split_suggest(1, 1, 500, 64, 1) == 1          # too short to split
+    assert lib.fa_split_suggest(4, 8, 1000, 64, 1) == 1         # a 19 us launch: a second launch costs more
+    assert lib.fa_split_suggest(1, 2, 4096, 128, 2) == 8        # 32 workgroups -> 256
     assert lib.fa_split_suggest(1, 1, 8192, 96, 2) == 1         # unsupported d
 
 

@@ -167,3 +167,20 @@ def test_merge_matches_oracle(dtype, d):
     print(f"merge {dtype} d{d}: max|dO| {eo:.3e} (tol {tol:.2e}) rel dLSE {el:.3e}", flush=True)
     assert np.isfinite(o).all() and eo <= tol
     assert np.all(lse[~live] == -np.inf) and el <= 2e-6
+
+
+def test_forward_with_suggested_splits():
+    """fa.forward(splits=None) takes the library's split count: two heads of
+    4096 keys fill 32 of 256 compute units unsplit, so it splits; the result
+    matches the oracle and the unsplit forward.  The ragged workload (a
+    19 us launch) stays unsplit: a second launch would cost more."""
+    w = inputs.WORKLOADS["ragged"]
+    assert fa.split_suggest(w.B, w.H, w.N, w.d, torch.float16) == 1
+    q, k, v = (t.to(DEV) for t in inputs.random_qkv((1, 2, 4096, 128), "bf16", 470))
+    assert fa.split_suggest(1, 2, 4096, 128, q.dtype) > 1
+    o, lse = fa.forward(q, k, v, splits=None)
+    o1, lse1 = fa.forward(q, k, v)
+    torch.cuda.synchronize()
+    ref_o, ref_lse = oracle.attention_ref(*(inputs.to_float64(t.cpu()) for t in (q, k, v)), f32(1 / np.sqrt(128)))
+    check(o.cpu(), lse.cpu(), ref_o, ref_lse, "bf16", "2 x 4096, suggested splits")
+    assert (o.float() - o1.float()).abs().max().item() <= 2e-2

@@ -154,8 +154,10 @@ extern "C" int64_t fa_split_suggest(int64_t B, int64_t H, int64_t N, int64_t d, 
     // Cost in 64-key tile steps of one workgroup: waves of workgroups times
     // (tiles per range + about 2 tiles of pipeline fill and epilogue), plus,
     // for S > 1, the merge's memory traffic (S partials read, O written) at
-    // about 12.6 MB per tile step (7 TB/s for one 1.8 us step).  Each range
-    // keeps at least 8 tiles (512 keys).
+    // about 12.6 MB per tile step (7 TB/s for one 1.8 us step) and a fixed
+    // 12 steps for the second launch and the partials' round trip (measured:
+    // a 19 us unsplit launch ran 28 us split in two).  Each range keeps at
+    // least 8 tiles (512 keys).
     int64_t most = tiles / 8;
     if (most > 64) most = 64;
     int64_t best = 1;
@@ -163,7 +165,7 @@ extern "C" int64_t fa_split_suggest(int64_t B, int64_t H, int64_t N, int64_t d, 
     for (int64_t s = 1; s <= (most > 1 ? most : 1); ++s) {
         const int64_t waves = (wg * s + slots - 1) / slots;
         double cost = (double)waves * (double)((tiles + s - 1) / s + 2);
-        if (s > 1) cost += (double)bh * (double)N * (double)d * (4.0 * s + 2.0) / 12.6e6;
+        if (s > 1) cost += 12.0 + (double)bh * (double)N * (double)d * (4.0 * s + 2.0) / 12.6e6;
         if (s == 1 || cost < best_cost) {
             best = s;
             best_cost = cost;

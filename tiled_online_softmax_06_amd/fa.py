@@ -233,8 +233,18 @@ def forward_fp8(q8, k8, v8, descale, scale: float | None = None, out_dtype=torch
     return o, lse
 
 
-def forward(q, k, v, scale: float | None = None):
-    """Returns (O, LSE): O like q, LSE float32 (B, H, N), natural log."""
+def forward(q, k, v, scale: float | None = None, splits: int | None = 1):
+    """Returns (O, LSE): O like q, LSE float32 (B, H, N), natural log.
+
+    splits: 1 runs fa_forward (one launch, no workspace); None takes the
+    library's suggested key-split count and, when that is above 1, runs
+    fa_forward_split with a workspace from torch (same result up to
+    rounding; faster when few heads leave compute units idle)."""
+    if splits is None:
+        B, H, N, d = q.shape
+        splits = split_suggest(B, H, N, d, q.dtype)
+    if splits > 1:
+        return forward_split(q, k, v, splits, scale)
     o = torch.empty_like(q)
     lse = torch.empty(q.shape[:3], dtype=torch.float32, device=q.device)
     forward_into(q, k, v, o, lse, scale)
