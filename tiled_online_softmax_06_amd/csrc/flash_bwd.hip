@@ -208,24 +208,46 @@ flash_bwd_dq(const T* __restrict__ Q, const T* __restrict__ K, const T* __restri
 #pragma unroll
     for (int dt = 0; dt < DT; ++dt) acc[dt] = f32x16(0.f);
 
+    // One K/V tile as a fixed program (sched_barrier between steps):
+    // S^T/dP^T steps (kt, kc) (two MFMAs each: K row x Q^T, V row x dO^T),
+    // the P^T/dS^T vector work, then dQ^T steps (pc, dt) (one MFMA each, K
+    // through the transpose read).  LDS operands run RQ steps ahead through
+    // `qring` (1 step for S/dP, 2 for dQ: deeper rings spill at d = 128);
+    // the first dQ^T operands are read before the vector work.
+    constexpr int RQ = 1;
+    u32x4 qring[2 * RQ];
     auto compute = [&](auto stage, int j0) {
         constexpr int st = decltype(stage)::value;
         const char* kb = st ? ks1 : ks0;
         const char* vb = st ? vs1 : vs0;
+        constexpr int N1 = KT * KC;
+        auto read1 = [&](auto step) {
+            constexpr int i = decltype(step)::value;
+            constexpr int kt = i / KC, kc = i % KC;
+            qring[2 * (i % RQ) + 0] = *(const u32x4*)(kb + (32 * kt + col) * ROWB + 16 * ((2 * kc) ^ kxr));
+            qring[2 * (i % RQ) + 1] = *(const u32x4*)(vb + (32 * kt + col) * ROWB + 16 * ((2 * kc) ^ vxr));
+        };
         // S^T = K Q^T and dP^T = V dO^T (keys x queries).
         f32x16 s[KT], dp[KT];
 #pragma unroll
-        for (int kt = 0; kt < KT; ++kt) {
-            s[kt] = f32x16(0.f);
-            dp[kt] = f32x16(0.f);
-#pragma unroll
-            for (int kc = 0; kc < KC; ++kc) {
-                const u32x4 a = *(const u32x4*)(kb + (32 * kt + col) * ROWB + 16 * ((2 * kc) ^ kxr));
-                s[kt] = M::run(a, qf[kc], s[kt]);
-                const u32x4 b = *(const u32x4*)(vb + (32 * kt + col) * ROWB + 16 * ((2 * kc) ^ vxr));
-                dp[kt] = M::run(b, of[kc], dp[kt]);
-            }
-        }
+        for (int kt = 0; kt < KT; ++kt) { s[kt] = f32x16(0.f); dp[kt] = f32x16(0.f); }
+        static_for<0, RQ>([&](auto i) { read1(i); });
+        static_for<0, N1>([&](auto step) {
+            constexpr int i = decltype(step)::value;
+            constexpr int kt = i / KC, kc = i % KC;
+            __builtin_amdgcn_sched_barrier(0);
+            s[kt] = M::run(qring[2 * (i % RQ) + 0], qf[kc], s[kt]);
+            dp[kt] = M::run(qring[2 * (i % RQ) + 1], of[kc], dp[kt]);
+            if constexpr (i + RQ < N1) read1(Int<i + RQ>{});
+        });
+        __builtin_amdgcn_sched_barrier(0);
+        constexpr int N2 = PC * DT;
+        auto read2 = [&](auto step) {
+            constexpr int i = decltype(step)::value;
+            constexpr int pc = i / DT, dt = i % DT;
+            qring[i % (2 * RQ)] = read_tr<ROWB>(kb, 16 * pc, ktr[dt]);
+        };
+        static_for<0, 2 * RQ>([&](auto i) { read2(i); });
         // P^T = exp2(S^T c - LSE log2 e); dS^T = P^T (dP^T - D).  Keys past
         // the end get P = 0.
         const bool tail = j0 + BC > n;
@@ -237,16 +259,23 @@ flash_bwd_dq(const T* __restrict__ Q, const T* __restrict__ K, const T* __restri
                 if (tail && j0 + 32 * kt + acc_row(r, half) >= n) pr = 0.f;
                 s[kt][r] = pr * (dp[kt][r] - dval);
             }
-        // dQ^T += K^T dS^T.
+        u32x4 bsv[PC];
 #pragma unroll
         for (int pc = 0; pc < PC; ++pc) {
             float w[8];
 #pragma unroll
             for (int e = 0; e < 8; ++e) w[e] = s[pc >> 1][8 * (pc & 1) + e];
-            const u32x4 b = M::pack(w);
-#pragma unroll
-            for (int dt = 0; dt < DT; ++dt) acc[dt] = M::run(read_tr<ROWB>(kb, 16 * pc, ktr[dt]), b, acc[dt]);
+            bsv[pc] = M::pack(w);
         }
+        // dQ^T += K^T dS^T.
+        static_for<0, N2>([&](auto step) {
+            constexpr int i = decltype(step)::value;
+            constexpr int pc = i / DT, dt = i % DT;
+            __builtin_amdgcn_sched_barrier(0);
+            acc[dt] = M::run(qring[i % (2 * RQ)], bsv[pc], acc[dt]);
+            if constexpr (i + 2 * RQ < N2) read2(Int<i + 2 * RQ>{});
+        });
+        __builtin_amdgcn_sched_barrier(0);
     };
 
     const int ntiles = (n + BC - 1) / BC;
@@ -394,21 +423,44 @@ flash_bwd_dkdv(const T* __restrict__ Q, const T* __restrict__ K, const T* __rest
 #pragma unroll
     for (int dt = 0; dt < DT; ++dt) { dka[dt] = f32x16(0.f); dva[dt] = f32x16(0.f); }
 
+    // One streamed tile as a fixed program (sched_barrier between steps):
+    // S/dP steps kc = 0..KC-1 (two MFMAs each: Q row x K, dO row x V), the
+    // P/dS vector work, then dV/dK steps (c2, dt) (two MFMAs each, operands
+    // from the transpose reads of dO and Q).  LDS operands run RB steps
+    // ahead through `ring` (deeper rings spill at d = 128); the first dV/dK
+    // operands are read before the vector work.
+    constexpr int RB = 1;
+    u32x4 ring[3 * RB];
     auto compute = [&](auto stage, int i0) {
         constexpr int st = decltype(stage)::value;
         const char* qb = st ? qs1 : qs0;
         const char* ob = st ? os1 : os0;
         const float* lb = st ? ls1 : ls0;
+        auto read1 = [&](auto step) {
+            constexpr int kc = decltype(step)::value;
+            ring[3 * (kc % RB) + 0] = *(const u32x4*)(qb + col * ROWB + 16 * ((2 * kc) ^ qxr));
+            ring[3 * (kc % RB) + 1] = *(const u32x4*)(ob + col * ROWB + 16 * ((2 * kc) ^ qxr));
+            ring[3 * (kc % RB) + 2] = *(const u32x4*)(vrow + 16 * ((2 * kc) ^ vxr));
+        };
         // S = Q K^T and dP = dO V^T (queries x keys).
         f32x16 s = f32x16(0.f), dp = f32x16(0.f);
-#pragma unroll
-        for (int kc = 0; kc < KC; ++kc) {
-            const u32x4 a = *(const u32x4*)(qb + col * ROWB + 16 * ((2 * kc) ^ qxr));
-            s = M::run(a, kf[kc], s);
-            const u32x4 a2 = *(const u32x4*)(ob + col * ROWB + 16 * ((2 * kc) ^ qxr));
-            const u32x4 vb = *(const u32x4*)(vrow + 16 * ((2 * kc) ^ vxr));
-            dp = M::run(a2, vb, dp);
-        }
+        static_for<0, RB>([&](auto i) { read1(i); });
+        static_for<0, KC>([&](auto step) {
+            constexpr int kc = decltype(step)::value;
+            __builtin_amdgcn_sched_barrier(0);
+            s = M::run(ring[3 * (kc % RB) + 0], kf[kc], s);
+            dp = M::run(ring[3 * (kc % RB) + 1], ring[3 * (kc % RB) + 2], dp);
+            if constexpr (kc + RB < KC) read1(Int<kc + RB>{});
+        });
+        __builtin_amdgcn_sched_barrier(0);
+        // dV/dK step i = c2 * DT + dt: operands tr(dO) and tr(Q), rows 16 c2.
+        auto read2 = [&](auto step) {
+            constexpr int i = decltype(step)::value;
+            constexpr int c2 = i / DT, dt = i % DT;
+            ring[2 * (i % RB) + 0] = read_tr<ROWB>(ob, 16 * c2, qtr[dt]);
+            ring[2 * (i % RB) + 1] = read_tr<ROWB>(qb, 16 * c2, qtr[dt]);
+        };
+        static_for<0, RB>([&](auto i) { read2(i); });
         // P = exp2(S c - LSE log2 e), dS = P (dP - D); register r holds query
         // row 8 (r / 4) + 4 half + r % 4: rows 8 q4 + 4 half .. +3 are four
         // consecutive floats.  Query rows past the end get P = dS = 0.
@@ -429,17 +481,18 @@ flash_bwd_dkdv(const T* __restrict__ Q, const T* __restrict__ K, const T* __rest
                 ds[r] = pr * (dp[r] - dv[e]);
             }
         }
+        const u32x4 bp[2] = {M::pack(&p[0]), M::pack(&p[8])};
+        const u32x4 bs[2] = {M::pack(&ds[0]), M::pack(&ds[8])};
         // dV^T += dO^T P and dK^T += Q^T dS (contraction over the 32 queries).
-#pragma unroll
-        for (int c2 = 0; c2 < 2; ++c2) {
-            const u32x4 bp = M::pack(&p[8 * c2]);
-            const u32x4 bs = M::pack(&ds[8 * c2]);
-#pragma unroll
-            for (int dt = 0; dt < DT; ++dt) {
-                dva[dt] = M::run(read_tr<ROWB>(ob, 16 * c2, qtr[dt]), bp, dva[dt]);
-                dka[dt] = M::run(read_tr<ROWB>(qb, 16 * c2, qtr[dt]), bs, dka[dt]);
-            }
-        }
+        static_for<0, 2 * DT>([&](auto step) {
+            constexpr int i = decltype(step)::value;
+            constexpr int c2 = i / DT, dt = i % DT;
+            __builtin_amdgcn_sched_barrier(0);
+            dva[dt] = M::run(ring[2 * (i % RB) + 0], bp[c2], dva[dt]);
+            dka[dt] = M::run(ring[2 * (i % RB) + 1], bs[c2], dka[dt]);
+            if constexpr (i + RB < 2 * DT) read2(Int<i + RB>{});
+        });
+        __builtin_amdgcn_sched_barrier(0);
     };
 
     // Stream (query head, query tile) pairs: heads g grp .. g grp + grp - 1.
