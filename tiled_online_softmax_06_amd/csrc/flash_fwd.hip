@@ -172,25 +172,53 @@ flash_fwd_16(const T* __restrict__ Q, const T* __restrict__ K, const T* __restri
     float mref = -INFINITY;   // reference max (log2 units of scaled scores)
     float lsum = 0.f;         // this lane's part of the row sum
 
+    // One tile as a fixed program (sched_barrier between steps): the S^T
+    // steps (kt, kc), one K read each, then the softmax, then the P.V steps
+    // (kt, c2, dt), two V transpose reads each.  LDS operands run R16 steps
+    // ahead through `ring`; the first P.V operands are read before the
+    // softmax so that they arrive while it runs.
+    constexpr int R16 = 4;
+    u32x4 ring[R16];
+    typedef short s16x4 __attribute__((ext_vector_type(4)));
+    typedef __attribute__((address_space(3))) s16x4* lds_s16x4;
     auto compute = [&](auto stage, int j0) {
         constexpr int st = decltype(stage)::value;
         const char* kb = st ? ks1 : ks0;
         const char* vb = st ? vs1 : vs0;
+        constexpr int N1 = KT * KC;
+        constexpr int N2 = KT * 2 * DT;
+        auto read1 = [&](auto step) {
+            constexpr int i = decltype(step)::value;
+            constexpr int kt = i / KC, kc = i % KC;
+            ring[i % R16] = *(const u32x4*)(kb + (32 * kt + col) * ROWB + 16 * ((2 * kc) ^ kx));
+        };
+        auto read2 = [&](auto step) {
+            constexpr int i = decltype(step)::value;
+            constexpr int kt = i / (2 * DT), c2 = (i / DT) % 2, dt = i % DT;
+            const char* vrow = vb + (32 * kt + 16 * c2) * ROWB;
+            const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4)(vrow + voff[dt]));
+            const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4)(vrow + 8 * ROWB + voff[dt]));
+            const u32x2 l2 = __builtin_bit_cast(u32x2, lo), h2 = __builtin_bit_cast(u32x2, hi);
+            ring[i % R16] = u32x4{l2.x, l2.y, h2.x, h2.y};
+        };
 
         // S^T = K Q^T (raw scores, fp32).
         f32x16 s[KT];
 #pragma unroll
-        for (int kt = 0; kt < KT; ++kt) {
-            s[kt] = f32x16(0.f);
-#pragma unroll
-            for (int kc = 0; kc < KC; ++kc) {
-                const u32x4 a = *(const u32x4*)(kb + (32 * kt + col) * ROWB + 16 * ((2 * kc) ^ kx));
-                s[kt] = M::run(a, qf[kc], s[kt]);
-            }
-        }
+        for (int kt = 0; kt < KT; ++kt) s[kt] = f32x16(0.f);
+        static_for<0, (R16 < N1 ? R16 : N1)>([&](auto i) { read1(i); });
+        static_for<0, N1>([&](auto step) {
+            constexpr int i = decltype(step)::value;
+            constexpr int kt = i / KC, kc = i % KC;
+            __builtin_amdgcn_sched_barrier(0);
+            s[kt] = M::run(ring[i % R16], qf[kc], s[kt]);
+            if constexpr (i + R16 < N1) read1(Int<i + R16>{});
+        });
+        __builtin_amdgcn_sched_barrier(0);
+        static_for<0, (R16 < N2 ? R16 : N2)>([&](auto i) { read2(i); });
 
-        const bool tail = j0 + BC > nk;
-        if (tail) {
+        const bool ragged = j0 + BC > nk;
+        if (ragged) {
 #pragma unroll
             for (int kt = 0; kt < KT; ++kt)
 #pragma unroll
@@ -218,7 +246,7 @@ flash_fwd_16(const T* __restrict__ Q, const T* __restrict__ K, const T* __restri
         for (int kt = 0; kt < KT; ++kt)
 #pragma unroll
             for (int r = 0; r < 16; ++r) s[kt][r] = __builtin_amdgcn_exp2f(fmaf(s[kt][r], c, -mref));
-        if (tail) {
+        if (ragged) {
 #pragma unroll
             for (int kt = 0; kt < KT; ++kt)
 #pragma unroll
@@ -232,28 +260,22 @@ flash_fwd_16(const T* __restrict__ Q, const T* __restrict__ K, const T* __restri
 
         // O^T += V^T P^T.  B operand: the lane's 8 weights of registers
         // 8*c2 .. 8*c2+7 (keys 16*c2 + {0..3, 8..11} + 4*half of the sub-tile).
-        // A operand: V at the same keys for dim 32*dt + col, two transpose
-        // reads of 4 keys each.
+        u32x4 pb[KT * 2];
 #pragma unroll
-        for (int kt = 0; kt < KT; ++kt) {
+        for (int j = 0; j < KT * 2; ++j) {
+            float pv[8];
 #pragma unroll
-            for (int c2 = 0; c2 < 2; ++c2) {
-                float pv[8];
-#pragma unroll
-                for (int e = 0; e < 8; ++e) pv[e] = s[kt][8 * c2 + e];
-                const u32x4 b = M::pack(pv);
-                const char* vrow = vb + (32 * kt + 16 * c2) * ROWB;
-#pragma unroll
-                for (int dt = 0; dt < DT; ++dt) {
-                    typedef short s16x4 __attribute__((ext_vector_type(4)));
-                    typedef __attribute__((address_space(3))) s16x4* lds_s16x4;
-                    const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4)(vrow + voff[dt]));
-                    const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4)(vrow + 8 * ROWB + voff[dt]));
-                    const u32x2 l2 = __builtin_bit_cast(u32x2, lo), h2 = __builtin_bit_cast(u32x2, hi);
-                    acc[dt] = M::run(u32x4{l2.x, l2.y, h2.x, h2.y}, b, acc[dt]);
-                }
-            }
+            for (int e = 0; e < 8; ++e) pv[e] = s[j >> 1][8 * (j & 1) + e];
+            pb[j] = M::pack(pv);
         }
+        static_for<0, N2>([&](auto step) {
+            constexpr int i = decltype(step)::value;
+            constexpr int j = i / DT, dt = i % DT;
+            __builtin_amdgcn_sched_barrier(0);
+            acc[dt] = M::run(ring[i % R16], pb[j], acc[dt]);
+            if constexpr (i + R16 < N2) read2(Int<i + R16>{});
+        });
+        __builtin_amdgcn_sched_barrier(0);
     };
 
     // Two LDS stages: while one is computed on, the DMA fills the other.
