@@ -72,6 +72,30 @@ def traffic_record(workload: str):
     return rec
 
 
+def device_info(props, peak_spec, fp8):
+    """Name, CU count and peak engine clock (hipDeviceGetAttribute), with the
+    dense MFMA peak derived from them (bf16/fp16: 4096 flop per clock per CU,
+    fp8 twice that) beside the published figure."""
+    import ctypes
+
+    info = {"name": props.name, "cu": props.multi_processor_count, "gcn_arch": getattr(props, "gcnArchName", "")}
+    try:
+        hip = ctypes.CDLL("libamdhip64.so")
+        val = ctypes.c_int(0)
+        dev = ctypes.c_int(0)
+        hip.hipGetDevice(ctypes.byref(dev))
+        # hipDeviceAttributeClockRate (kHz): the sixth entry of hipDeviceAttribute_t
+        if hip.hipDeviceGetAttribute(ctypes.byref(val), 5, dev.value) == 0 and 1e5 < val.value < 1e7:
+            ghz = val.value / 1e6
+            per_clk = 4096 * (2 if fp8 else 1)
+            info["peak_clock_ghz"] = round(ghz, 3)
+            info["derived_peak_tflops"] = round(props.multi_processor_count * ghz * 1e9 * per_clk / 1e12, 1)
+            info["published_peak_tflops"] = peak_spec
+    except OSError:
+        pass
+    return info
+
+
 def cpu_baseline_backward(w, q, k, v, do, heads: int, workers: int):
     """The backward oracle, untuned, on a bounded sample: the first `heads`
     (b, h) heads of the workload (whole heads: every query and key), one head
@@ -106,6 +130,44 @@ def cpu_baseline_backward(w, q, k, v, do, heads: int, workers: int):
             "sample": f"first {heads} of {w.B * w.H} heads, every query and key "
                       f"({flops / 1e9:.1f} GFLOP counted as 10*N^2*d per head, float64)",
             "seconds": round(dt, 3)}
+
+
+def cpu_baseline_rows(w, q, k, v, workers: int, gpu_out=None):
+    """The oracle on the workload's seeded sample of query rows (workloads
+    whose parity is checked on sampled rows), one row chunk per worker, with
+    the full-workload time extrapolated from it and labelled as such."""
+    from concurrent.futures import ThreadPoolExecutor
+
+    import numpy as np
+    from threadpoolctl import threadpool_limits
+
+    import oracle
+    from tiled_online_softmax_06_amd import inputs
+
+    rows = inputs.sample_rows(w)
+    q64, k64, v64 = (inputs.to_float64(t) for t in (q, k, v))
+    scale = float(np.float32(w.scale))
+    parts = np.array_split(rows, workers)
+    with threadpool_limits(1):
+        t0 = time.perf_counter()
+        with ThreadPoolExecutor(max_workers=workers) as ex:
+            results = list(ex.map(lambda r: (r, oracle.attention_ref(q64, k64, v64, scale, rows=r)), parts))
+        dt = time.perf_counter() - t0
+    flops = 4 * rows.size * w.N * w.d
+    out = {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": workers, "kind": "oracle",
+           "sample": f"{rows.size} seeded query rows of {w.B * w.H * w.N} (default_rng(2005)), each against "
+                     f"its head's {w.N} keys ({flops / 1e9:.2f} GFLOP in float64)",
+           "seconds": round(dt, 3),
+           "extrapolated_full_workload_seconds": round(dt * w.flops / flops, 1)}
+    if gpu_out is not None:
+        o_gpu = gpu_out[0].reshape(-1, w.d)
+        lse_gpu = gpu_out[1].reshape(-1)
+        eo = el = 0.0
+        for r, (o_ref, lse_ref) in results:
+            eo = max(eo, float(np.abs(o_gpu[r].double().numpy() - o_ref).max()))
+            el = max(el, float(np.abs(lse_gpu[r].double().numpy() - lse_ref).max()))
+        out["sample_max_abs_err"] = {"O": eo, "LSE": el}
+    return out
 
 
 def cpu_baseline(w, q, k, v, heads: int, chunk: int, workers: int, gpu_out=None):
@@ -272,6 +334,19 @@ def main():
     torch.cuda.synchronize()
     ms = start.elapsed_time(end) / max(args.steps, 1)
 
+    # Per-launch spread, after and outside the timed region: each launch
+    # bracketed by its own pair of events on the launch stream.
+    per = []
+    for _ in range(min(args.steps, 50)):
+        a = torch.cuda.Event(enable_timing=True)
+        b = torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        step()
+        b.record(stream)
+        per.append((a, b))
+    torch.cuda.synchronize()
+    per_ms = sorted(a.elapsed_time(b) for a, b in per)
+
     flops = w.flops
     if backward:
         flops = 10 * w.B * w.H * w.N * w.N * w.d
@@ -314,8 +389,10 @@ def main():
                    "B": w.B, "H": w.H, "N": w.N, "d": w.d, "causal": False, "kv_heads": kv_heads},
         "pct_of_mfma_peak": round(100 * tflops / peak, 2),
         "roofline": roof,
-        "device": {"name": props.name, "cu": props.multi_processor_count,
-                   "gcn_arch": getattr(props, "gcnArchName", "")},
+        "launch_ms": ({"median": round(per_ms[len(per_ms) // 2], 5), "min": round(per_ms[0], 5),
+                       "max": round(per_ms[-1], 5), "n": len(per_ms),
+                       "note": "separately evented launches after the timed region"} if per_ms else None),
+        "device": device_info(props, peak, fp8),
         "kernel_sha256_16": kernel_hash(BWD_SOURCE if backward else (FP8_SOURCE if fp8 else KERNEL_SOURCE)),
     }
     if backward:
@@ -338,6 +415,9 @@ def main():
     elif not args.no_cpu_baseline and backward:
         workers = max(1, min(16, len(os.sched_getaffinity(0))))
         result["cpu_baseline"] = cpu_baseline_backward(w, q, k, v, do, args.cpu_heads or min(8, workers), workers)
+    elif not args.no_cpu_baseline and w.sample_rows and not args.seq_len:
+        workers = max(1, min(16, len(os.sched_getaffinity(0))))
+        result["cpu_baseline"] = cpu_baseline_rows(w, q, k, v, workers, gpu_out=(o.cpu(), lse.cpu()))
     elif not args.no_cpu_baseline:
         workers = max(1, min(16, len(os.sched_getaffinity(0))))
         chunk = 512 if w.N >= 4096 else max(64, w.N // 4)
