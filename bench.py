@@ -48,8 +48,13 @@ BWD_SOURCE = os.path.join(HERE, "tiled_online_softmax_06_amd", "csrc", "flash_bw
 
 
 def kernel_hash(path: str = KERNEL_SOURCE) -> str:
+    """First 16 hex digits of sha256 over a kernel source and the compiler
+    flags it is built with (paths left out), so a record taken on another
+    build of the kernel is not used."""
+    from tiled_online_softmax_06_amd import build_lib
+    flags = " ".join(f for f in build_lib.FLAGS if "/" not in f and f != "-I")
     with open(path, "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()[:16]
+        return hashlib.sha256(f.read() + flags.encode()).hexdigest()[:16]
 
 
 def kernel_name(w) -> str:

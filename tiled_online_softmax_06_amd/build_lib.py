@@ -26,6 +26,9 @@ FLAGS = [
     "-shared",
     # no packed fp32 VALU instructions in device code
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    # device code never tests for NaN: max/min need no quieting of their
+    # inputs (the host side keeps its isfinite checks of the arguments)
+    "-Xarch_device", "-fno-honor-nans",
     "-I", os.path.join(ROOT, "include"),
 ]
 
