@@ -249,16 +249,27 @@ flash_bwd_dq(const T* __restrict__ Q, const T* __restrict__ K, const T* __restri
         };
         static_for<0, 2 * RQ>([&](auto i) { read2(i); });
         // P^T = exp2(S^T c - LSE log2 e); dS^T = P^T (dP^T - D).  Keys past
-        // the end get P = 0.
-        const bool tail = j0 + BC > n;
+        // the end (clamped rows of a ragged last tile) get dS = 0, in a branch
+        // taken by that tile only: one limit per sub-tile against the
+        // registers' constant row offsets, and the empty volatile asm keeps the
+        // compiler from turning it into selects that every tile executes.
 #pragma unroll
         for (int kt = 0; kt < KT; ++kt)
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
-                float pr = __builtin_amdgcn_exp2f(fmaf(s[kt][r], c, -lse2));
-                if (tail && j0 + 32 * kt + acc_row(r, half) >= n) pr = 0.f;
+                const float pr = __builtin_amdgcn_exp2f(fmaf(s[kt][r], c, -lse2));
                 s[kt][r] = pr * (dp[kt][r] - dval);
             }
+        if (j0 + BC > n) {
+            asm volatile("");
+#pragma unroll
+            for (int kt = 0; kt < KT; ++kt) {
+                const int lim = n - j0 - 32 * kt - 4 * half;
+#pragma unroll
+                for (int r = 0; r < 16; ++r)
+                    if (8 * (r >> 2) + (r & 3) >= lim) s[kt][r] = 0.f;
+            }
+        }
         u32x4 bsv[PC];
 #pragma unroll
         for (int pc = 0; pc < PC; ++pc) {
@@ -463,8 +474,9 @@ flash_bwd_dkdv(const T* __restrict__ Q, const T* __restrict__ K, const T* __rest
         static_for<0, RB>([&](auto i) { read2(i); });
         // P = exp2(S c - LSE log2 e), dS = P (dP - D); register r holds query
         // row 8 (r / 4) + 4 half + r % 4: rows 8 q4 + 4 half .. +3 are four
-        // consecutive floats.  Query rows past the end get P = dS = 0.
-        const bool tail = i0 + BQ > n;
+        // consecutive floats.  Query rows past the end get P = dS = 0 (set,
+        // not multiplied: their LSE and D slots need not be finite), in a
+        // branch taken by a ragged last query block only (see the dQ kernel).
         float p[16], ds[16];
 #pragma unroll
         for (int q4 = 0; q4 < 4; ++q4) {
@@ -475,11 +487,20 @@ flash_bwd_dkdv(const T* __restrict__ Q, const T* __restrict__ K, const T* __rest
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
                 const int r = 4 * q4 + e;
-                float pr = __builtin_amdgcn_exp2f(fmaf(s[r], c, -lv[e]));
-                if (tail && i0 + 8 * q4 + 4 * half + e >= n) pr = 0.f;
+                const float pr = __builtin_amdgcn_exp2f(fmaf(s[r], c, -lv[e]));
                 p[r] = pr;
                 ds[r] = pr * (dp[r] - dv[e]);
             }
+        }
+        if (i0 + BQ > n) {
+            asm volatile("");
+            const int lim = n - i0 - 4 * half;
+#pragma unroll
+            for (int r = 0; r < 16; ++r)
+                if (8 * (r >> 2) + (r & 3) >= lim) {
+                    p[r] = 0.f;
+                    ds[r] = 0.f;
+                }
         }
         const u32x4 bp[2] = {M::pack(&p[0]), M::pack(&p[8])};
         const u32x4 bs[2] = {M::pack(&ds[0]), M::pack(&ds[8])};

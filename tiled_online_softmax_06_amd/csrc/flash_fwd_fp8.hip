@@ -203,21 +203,29 @@ flash_fwd_fp8(const uint8_t* __restrict__ Q, const uint8_t* __restrict__ K, cons
             }
         }
 
-        const bool tail = j0 + BC > n;
-        if (tail) {
+        // Keys past the end of a ragged last tile get score -inf, hence weight
+        // exp2(-inf) = 0 (c is never 0).  One limit per sub-tile is compared
+        // with the registers' constant row offsets; the empty volatile asm
+        // keeps the block a branch (otherwise it is turned into selects that
+        // every tile executes).
+        if (j0 + BC > n) {
+            asm volatile("");
 #pragma unroll
-            for (int kt = 0; kt < KT; ++kt)
+            for (int kt = 0; kt < KT; ++kt) {
+                const int lim = n - j0 - 32 * kt - 4 * half;
 #pragma unroll
                 for (int r = 0; r < 16; ++r)
-                    if (j0 + 32 * kt + acc_row(r, half) >= n) s[kt][r] = -INFINITY;
+                    if (8 * (r >> 2) + (r & 3) >= lim) s[kt][r] = -INFINITY;
+            }
         }
 
-        float mt = -INFINITY;
+        // Tile max in four independent chains (one per group of 4 registers).
+        float mp[4] = {-INFINITY, -INFINITY, -INFINITY, -INFINITY};
 #pragma unroll
         for (int kt = 0; kt < KT; ++kt)
 #pragma unroll
-            for (int r = 0; r < 16; ++r) mt = fmaxf(mt, s[kt][r]);
-        mt = pair_max(mt) * c;
+            for (int r = 0; r < 16; ++r) mp[r >> 2] = fmaxf(mp[r >> 2], s[kt][r]);
+        const float mt = pair_max(fmaxf(fmaxf(mp[0], mp[1]), fmaxf(mp[2], mp[3]))) * c;
 
         // The reference moves only when a tile max exceeds it by more than
         // kFp8Slack (log2 units; 2^8.75 < 448, e4m3's largest value), and
@@ -237,17 +245,12 @@ flash_fwd_fp8(const uint8_t* __restrict__ Q, const uint8_t* __restrict__ K, cons
         for (int kt = 0; kt < KT; ++kt)
 #pragma unroll
             for (int r = 0; r < 16; ++r) s[kt][r] = __builtin_amdgcn_exp2f(fmaf(s[kt][r], c, -mref));
-        if (tail) {
-#pragma unroll
-            for (int kt = 0; kt < KT; ++kt)
-#pragma unroll
-                for (int r = 0; r < 16; ++r)
-                    if (j0 + 32 * kt + acc_row(r, half) >= n) s[kt][r] = 0.f;
-        }
+        float part[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int kt = 0; kt < KT; ++kt)
 #pragma unroll
-            for (int r = 0; r < 16; ++r) lsum += s[kt][r];
+            for (int r = 0; r < 16; ++r) part[r & 3] += s[kt][r];
+        lsum += (part[0] + part[1]) + (part[2] + part[3]);
 
         // P^T as the B operand: dword (kt, q) holds keys 32 kt + 8 q + 4 half
         // + 0..3; swapping the upper half of dword 2p with the lower half of
