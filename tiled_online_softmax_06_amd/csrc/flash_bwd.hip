@@ -438,9 +438,11 @@ flash_bwd_dkdv(const T* __restrict__ Q, const T* __restrict__ K, const T* __rest
     // S/dP steps kc = 0..KC-1 (two MFMAs each: Q row x K, dO row x V), the
     // P/dS vector work, then dV/dK steps (c2, dt) (two MFMAs each, operands
     // from the transpose reads of dO and Q).  LDS operands run RB steps
-    // ahead through `ring` (deeper rings spill at d = 128); the first dV/dK
-    // operands are read before the vector work.
-    constexpr int RB = 1;
+    // ahead through `ring`: two at d = 128 (3-6 % faster than one, for a few
+    // more spilled scalars; three spill inside the loop), one at d = 64 (two
+    // are 24 % slower there); the first dV/dK operands are read before the
+    // vector work.
+    constexpr int RB = D == 128 ? 2 : 1;
     u32x4 ring[3 * RB];
     auto compute = [&](auto stage, int i0) {
         constexpr int st = decltype(stage)::value;
