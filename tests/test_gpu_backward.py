@@ -74,10 +74,11 @@ def full_case(B, H, Hkv, N, d, dtype, seed, scale=None):
 
 @pytest.mark.parametrize("dtype", ["fp16", "bf16"])
 @pytest.mark.parametrize("d", [64, 128])
-@pytest.mark.parametrize("N", [1, 77, 256, 300])
+@pytest.mark.parametrize("N", [1, 65, 77, 256, 300])
 def test_backward_ragged_lengths(dtype, d, N):
-    """Lengths below one tile, one short of a 32-row block boundary, exact
-    tiles and a ragged tail over several tiles."""
+    """Lengths below one tile, a last key tile and a last 32-row query block
+    holding a single valid row (N = 65), a ragged block, exact tiles and a
+    ragged tail over several tiles."""
     full_case(1, 2, 2, N, d, dtype, seed=50 + N + d)
 
 

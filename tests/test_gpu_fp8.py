@@ -77,8 +77,10 @@ def fp8_case(B, H, Hkv, N, d, seed, out="bf16", scale=None, sigma=1.0):
 
 
 @pytest.mark.parametrize("d", [64, 128])
-@pytest.mark.parametrize("N", [1, 77, 256, 1000])
+@pytest.mark.parametrize("N", [1, 65, 77, 256, 1000])
 def test_fp8_matches_oracle(d, N):
+    """N = 65: the last 64-key tile holds a single valid key (the masking
+    branch with every other key of both 32-key sub-tiles past the end)."""
     fp8_case(1, 2, 2, N, d, seed=500 + N + d)
 
 
