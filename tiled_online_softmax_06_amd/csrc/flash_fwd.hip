@@ -493,6 +493,10 @@ flash_fwd_pp(const T* __restrict__ Q, const T* __restrict__ K, const T* __restri
                 acc[dt] = M::run(ring[i % R], p[pc], acc[dt]);
             }
         };
+        // The wave in its MFMA phase takes issue priority over the softmax-phase
+        // wave on the same SIMD, so a product whose operands are ready is not
+        // held behind the other wave's vector instructions.
+        __builtin_amdgcn_s_setprio(1);
         if constexpr (!decltype(filled)::value) static_for<0, (R < NS ? R : NS)>([&](auto i) { read(i); });
         static_for<0, NS>([&](auto i) {
             constexpr int k = decltype(i)::value;
@@ -500,6 +504,8 @@ flash_fwd_pp(const T* __restrict__ Q, const T* __restrict__ K, const T* __restri
             mma(i);
             if constexpr (k + R < NS) read(Int<k + R>{});
         });
+        __builtin_amdgcn_sched_barrier(0);
+        __builtin_amdgcn_s_setprio(0);
         __builtin_amdgcn_sched_barrier(0);
     };
     // First R K operands of an MFMA phase, read ahead at the end of the
@@ -544,14 +550,16 @@ flash_fwd_pp(const T* __restrict__ Q, const T* __restrict__ K, const T* __restri
             for (int dt = 0; dt < DT; ++dt) acc[dt] *= alpha;
             mref = mnew;
         }
-        float part[4] = {0.f, 0.f, 0.f, 0.f};
+        // Row sum of the unrounded weights in four chains (the first weight of
+        // each chain starts it: no 0 + x adds).
+        float part[4];
 #pragma unroll
         for (int kt = 0; kt < KT; ++kt)
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
                 const float e = __builtin_amdgcn_exp2f(fmaf(s[kt][r], c, -mref));
                 s[kt][r] = e;
-                part[r & 3] += e;
+                part[r & 3] = (kt == 0 && r < 4) ? e : part[r & 3] + e;
             }
         lsum += (part[0] + part[1]) + (part[2] + part[3]);
 #pragma unroll
@@ -607,25 +615,20 @@ flash_fwd_pp(const T* __restrict__ Q, const T* __restrict__ K, const T* __restri
     phase_barrier();
     prefetch(ks0);
     if (group == 1) phase_barrier();     // group B runs one phase behind
-    if (ntiles == 1) {
-        pair(0, Int<0>{}, Tr{}, F{}, F{});
-        pair(1, Int<1>{}, F{}, Tr{}, F{});
+    // The last full pair of the loop may prefetch K operands of a tile that
+    // does not exist (stale LDS, never used: the phase after it has no Q.K^T
+    // products); this keeps one tail per tile-count parity.
+    pair(0, Int<0>{}, Tr{}, F{}, Tr{});
+    int j = 1;
+    for (; j + 1 < ntiles; j += 2) {
+        pair(j, Int<1>{}, Tr{}, Tr{}, Tr{});
+        pair(j + 1, Int<0>{}, Tr{}, Tr{}, Tr{});
+    }
+    if (j < ntiles) {
+        pair(j, Int<1>{}, Tr{}, Tr{}, F{});
+        pair(j + 1, Int<0>{}, F{}, Tr{}, F{});
     } else {
-        pair(0, Int<0>{}, Tr{}, F{}, Tr{});
-        int j = 1;
-        for (; j + 2 < ntiles; j += 2) {
-            pair(j, Int<1>{}, Tr{}, Tr{}, Tr{});
-            pair(j + 1, Int<0>{}, Tr{}, Tr{}, Tr{});
-        }
-        // j odd; j == ntiles - 2 or ntiles - 1
-        if (j == ntiles - 2) {
-            pair(j, Int<1>{}, Tr{}, Tr{}, Tr{});
-            pair(j + 1, Int<0>{}, Tr{}, Tr{}, F{});
-            pair(j + 2, Int<1>{}, F{}, Tr{}, F{});
-        } else {
-            pair(j, Int<1>{}, Tr{}, Tr{}, F{});
-            pair(j + 1, Int<0>{}, F{}, Tr{}, F{});
-        }
+        pair(j, Int<1>{}, F{}, Tr{}, F{});
     }
     if (group == 0) phase_barrier();
 
