@@ -518,10 +518,17 @@ flash_fwd_pp(const T* __restrict__ Q, const T* __restrict__ K, const T* __restri
         });
     };
 
-    // Online softmax of one tile (in place on s, packed into p).  Keys past
-    // the end of a ragged last tile get score -inf, hence weight 0 (the host
-    // never passes c = 0, so -inf * c stays -inf).
-    auto softmax = [&](int j0) {
+    // Online softmax of one tile (scores in s, weights packed into p).  Keys
+    // past the end of a ragged last tile get score -inf, hence weight 0 (the
+    // host never passes c = 0, so -inf * c stays -inf).
+    // The weights are first taken against the current reference max, without
+    // this tile's max: only when some lane's sum of them exceeds
+    // kTileSumLimit is the reference raised to the tile max (the output and
+    // sum rescaled) and the weights taken again.  The first tile always
+    // raises it.  So every weight stays <= kTileSumLimit, and the tile max
+    // (about 20 vector instructions per tile) is computed only on the rare
+    // tiles that need it.
+    auto softmax = [&](int j0, auto first) {
         if (j0 + BC > nk) {
 #pragma unroll
             for (int kt = 0; kt < KT; ++kt) {
@@ -531,44 +538,53 @@ flash_fwd_pp(const T* __restrict__ Q, const T* __restrict__ K, const T* __restri
                     if (8 * (r >> 2) + (r & 3) >= lim) s[kt][r] = -INFINITY;
             }
         }
-        float mp[4];
+        // Raise the reference max to this tile's max (both lanes of a query
+        // pair agree) and rescale the running sum and output by
+        // exp2(m_old - m_new).
+        auto raise = [&](auto first) {
+            float mp[4];
 #pragma unroll
-        for (int q = 0; q < 4; ++q) mp[q] = fmaxf(s[q >> 1][8 * (q & 1)], s[q >> 1][8 * (q & 1) + 1]);
+            for (int q = 0; q < 4; ++q) mp[q] = fmaxf(s[q >> 1][8 * (q & 1)], s[q >> 1][8 * (q & 1) + 1]);
 #pragma unroll
-        for (int kt = 0; kt < KT; ++kt)
+            for (int kt = 0; kt < KT; ++kt)
 #pragma unroll
-            for (int r = 2; r < 16; ++r) {
-                const int q = 2 * kt + (r >> 3);
-                if ((r & 7) >= 2) mp[q] = fmaxf(mp[q], s[kt][r]);
-            }
-        const float mt = pair_max(fmaxf(fmaxf(mp[0], mp[1]), fmaxf(mp[2], mp[3]))) * c;
-        if (__ballot(mt > mref + kRescaleSlack)) {
+                for (int r = 2; r < 16; ++r) {
+                    const int q = 2 * kt + (r >> 3);
+                    if ((r & 7) >= 2) mp[q] = fmaxf(mp[q], s[kt][r]);
+                }
+            const float mt = pair_max(fmaxf(fmaxf(mp[0], mp[1]), fmaxf(mp[2], mp[3]))) * c;
             const float mnew = fmaxf(mref, mt);
-            const float alpha = __builtin_amdgcn_exp2f(mref - mnew);
-            lsum *= alpha;
+            if constexpr (!decltype(first)::value) {
+                const float alpha = __builtin_amdgcn_exp2f(mref - mnew);
+                lsum *= alpha;
 #pragma unroll
-            for (int dt = 0; dt < DT; ++dt) acc[dt] *= alpha;
-            mref = mnew;
-        }
-        // Row sum of the unrounded weights in four chains (the first weight of
-        // each chain starts it: no 0 + x adds).
-        float part[4];
-#pragma unroll
-        for (int kt = 0; kt < KT; ++kt)
-#pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                const float e = __builtin_amdgcn_exp2f(fmaf(s[kt][r], c, -mref));
-                s[kt][r] = e;
-                part[r & 3] = (kt == 0 && r < 4) ? e : part[r & 3] + e;
+                for (int dt = 0; dt < DT; ++dt) acc[dt] *= alpha;
             }
-        lsum += (part[0] + part[1]) + (part[2] + part[3]);
+            mref = mnew;
+        };
+        // Weights exp2(s c - m) packed into p; returns this lane's sum of the
+        // unrounded weights (four chains, each started by its first weight).
+        auto weights = [&]() {
+            float part[4];
 #pragma unroll
-        for (int pc = 0; pc < PC; ++pc) {
-            float w[8];
+            for (int pc = 0; pc < PC; ++pc) {
+                float w[8];
 #pragma unroll
-            for (int e = 0; e < 8; ++e) w[e] = s[pc >> 1][8 * (pc & 1) + e];
-            p[pc] = M::pack(w);
+                for (int e = 0; e < 8; ++e) {
+                    w[e] = __builtin_amdgcn_exp2f(fmaf(s[pc >> 1][8 * (pc & 1) + e], c, -mref));
+                    part[e & 3] = (pc == 0 && e < 4) ? w[e] : part[e & 3] + w[e];
+                }
+                p[pc] = M::pack(w);
+            }
+            return (part[0] + part[1]) + (part[2] + part[3]);
+        };
+        if constexpr (decltype(first)::value) raise(Int<1>{});
+        float t = weights();
+        if (__ballot(t > kTileSumLimit)) {
+            raise(Int<0>{});
+            t = weights();
         }
+        lsum += t;
         // keep the whole softmax inside its phase
 #pragma unroll
         for (int pc = 0; pc < PC; ++pc) asm volatile("" : "+v"(p[pc]));
@@ -599,7 +615,8 @@ flash_fwd_pp(const T* __restrict__ Q, const T* __restrict__ K, const T* __restri
         } else {
             if (j + 2 < ntiles) issue(krs, kcur, (j + 2) * BC, Int<1>{});
         }
-        if constexpr (decltype(has_qk)::value) softmax(j * BC);
+        // tile 0's phase pair is the only one with Q.K^T and no P.V products
+        if constexpr (decltype(has_qk)::value) softmax(j * BC, Int<!decltype(has_pv)::value>{});
         if constexpr (decltype(pf)::value) prefetch(knxt);
         __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0): this wave's loads landed
         phase_barrier();
