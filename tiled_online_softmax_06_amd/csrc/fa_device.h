@@ -20,9 +20,9 @@ constexpr float kLn2 = 0.693147180559945309f;
 // The reference max is raised only when a tile max exceeds it by more than
 // this (log2 units): weights stay <= 2^8, well inside fp16/bf16/fp32 range.
 constexpr float kRescaleSlack = 8.0f;
-// Bound on one lane's sum of a tile's weights before the d = 128 forward
-// raises its reference max: weights stay <= 2^12, inside fp16 range for the
-// P.V operand.
+// Bound on one lane's sum of a tile's weights before the fp16/bf16 forward
+// kernels raise their reference max: weights stay <= 2^12, inside fp16 range
+// for the P.V operand.
 constexpr float kTileSumLimit = 4096.0f;
 
 template <typename T> struct Mfma;

@@ -19,11 +19,14 @@
 //      transpose puts one query per lane, so the row max and row sum are
 //      in-lane reductions plus one cross-half swap.
 //   3. Keys >= N in a ragged last tile are masked.
-//   4. Row max; the running reference max is raised (and the accumulators
-//      rescaled by exp(m_old - m_new)) only when the tile max exceeds it by
-//      more than 2^8 in weight, so the rescale is rare after the first tiles.
-//   5. p = exp2(s * c - m) with c = scale * log2(e): one FMA and one v_exp_f32
-//      per score.
+//   4. p = exp2(s * c - m) with c = scale * log2(e): one FMA and one v_exp_f32
+//      per score, against the running reference max m.
+//   5. m is raised to the tile's row max (the accumulators rescaled by
+//      exp2(m_old - m_new), the weights taken again) only when it has to be:
+//      fp16/bf16 kernels, when a lane's sum of the tile's weights exceeds
+//      2^12 (and on the first tile); fp32 kernel, when the tile max exceeds
+//      m by more than 2^8 in weight.  So the rescale, and in the 16-bit
+//      kernels the tile max itself, are rare after the first tiles.
 //   6. O^T += V^T P^T on MFMA; P goes straight from the accumulator registers
 //      into the B operand (rounded to the input type for fp16/bf16), V^T is
 //      read with the LDS transpose read ds_read_b64_tr_b16.
@@ -226,48 +229,50 @@ flash_fwd_16(const T* __restrict__ Q, const T* __restrict__ K, const T* __restri
                     if (j0 + 32 * kt + acc_row(r, half) >= nk) s[kt][r] = -INFINITY;
         }
 
-        float mt = -INFINITY;
-#pragma unroll
-        for (int kt = 0; kt < KT; ++kt)
-#pragma unroll
-            for (int r = 0; r < 16; ++r) mt = fmaxf(mt, s[kt][r]);
-        mt = pair_max(mt) * c;
-
-        if (__ballot(mt > mref + kRescaleSlack)) {
-            const float mnew = fmaxf(mref, mt);
-            const float alpha = __builtin_amdgcn_exp2f(mref - mnew);
-            lsum *= alpha;
-#pragma unroll
-            for (int dt = 0; dt < DT; ++dt) acc[dt] *= alpha;
-            mref = mnew;
-        }
-
-#pragma unroll
-        for (int kt = 0; kt < KT; ++kt)
-#pragma unroll
-            for (int r = 0; r < 16; ++r) s[kt][r] = __builtin_amdgcn_exp2f(fmaf(s[kt][r], c, -mref));
-        if (ragged) {
+        // Weights against the current reference max first; the tile max, the
+        // rescale of the output and sum by exp2(m_old - m_new) and a second
+        // pass only when a lane's sum of them exceeds kTileSumLimit (and on
+        // the first tile, where the reference is still -inf).
+        auto raise = [&](bool first) {
+            float mt = -INFINITY;
 #pragma unroll
             for (int kt = 0; kt < KT; ++kt)
 #pragma unroll
-                for (int r = 0; r < 16; ++r)
-                    if (j0 + 32 * kt + acc_row(r, half) >= nk) s[kt][r] = 0.f;
-        }
+                for (int r = 0; r < 16; ++r) mt = fmaxf(mt, s[kt][r]);
+            const float mnew = fmaxf(mref, pair_max(mt) * c);
+            if (!first) {
+                const float alpha = __builtin_amdgcn_exp2f(mref - mnew);
+                lsum *= alpha;
 #pragma unroll
-        for (int kt = 0; kt < KT; ++kt)
-#pragma unroll
-            for (int r = 0; r < 16; ++r) lsum += s[kt][r];
-
+                for (int dt = 0; dt < DT; ++dt) acc[dt] *= alpha;
+            }
+            mref = mnew;
+        };
         // O^T += V^T P^T.  B operand: the lane's 8 weights of registers
         // 8*c2 .. 8*c2+7 (keys 16*c2 + {0..3, 8..11} + 4*half of the sub-tile).
+        // Returns the lane's sum of the unrounded weights (four chains).
         u32x4 pb[KT * 2];
+        auto weights = [&]() {
+            float part[4];
 #pragma unroll
-        for (int j = 0; j < KT * 2; ++j) {
-            float pv[8];
+            for (int j = 0; j < KT * 2; ++j) {
+                float pv[8];
 #pragma unroll
-            for (int e = 0; e < 8; ++e) pv[e] = s[j >> 1][8 * (j & 1) + e];
-            pb[j] = M::pack(pv);
+                for (int e = 0; e < 8; ++e) {
+                    pv[e] = __builtin_amdgcn_exp2f(fmaf(s[j >> 1][8 * (j & 1) + e], c, -mref));
+                    part[e & 3] = (j == 0 && e < 4) ? pv[e] : part[e & 3] + pv[e];
+                }
+                pb[j] = M::pack(pv);
+            }
+            return (part[0] + part[1]) + (part[2] + part[3]);
+        };
+        if (j0 == 0) raise(true);
+        float t = weights();
+        if (__ballot(t > kTileSumLimit)) {
+            raise(false);
+            t = weights();
         }
+        lsum += t;
         static_for<0, N2>([&](auto step) {
             constexpr int i = decltype(step)::value;
             constexpr int j = i / DT, dt = i % DT;
