@@ -152,17 +152,35 @@ def test_scales(scale):
     check(o, lse, ref_o, ref_lse, "bf16", f"scale={scale}")
 
 
-def test_large_logits_rescaling():
+@pytest.mark.parametrize("d", [64, 128])
+def test_large_logits_rescaling(d):
     """Logits with std ~ 9 (Q, K ~ N(0, 3), V ~ N(0, 1)) and increasing row
     max along the keys (keys sorted by q.k for one query) force repeated
     rescaling of the running state."""
-    q, k, _ = inputs.random_qkv((1, 2, 1536, 128), "bf16", seed=11, sigma=3.0)
-    _, _, v = inputs.random_qkv((1, 2, 1536, 128), "bf16", seed=12)
+    q, k, _ = inputs.random_qkv((1, 2, 1536, d), "bf16", seed=11, sigma=3.0)
+    _, _, v = inputs.random_qkv((1, 2, 1536, d), "bf16", seed=12)
     order = torch.argsort((k.float() @ q.float()[0, 0, 0]).reshape(2, -1)[0])
     k = k[:, :, order].contiguous()
-    o, lse = run(q, k, v, 1 / math.sqrt(128))
-    ref_o, ref_lse = oracle_full(q, k, v, 1 / math.sqrt(128))
-    check(o, lse, ref_o, ref_lse, "bf16", "large logits")
+    o, lse = run(q, k, v, 1 / math.sqrt(d))
+    ref_o, ref_lse = oracle_full(q, k, v, 1 / math.sqrt(d))
+    check(o, lse, ref_o, ref_lse, "bf16", f"large logits d={d}")
+
+
+@pytest.mark.parametrize("dtype", ["fp16", "bf16"])
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("pos", [600, 997])
+def test_late_score_spike(dtype, d, pos):
+    """One key far above every earlier score (about 130 binades for the
+    largest queries: its weight against the running reference overflows
+    float32) in a middle tile or in the ragged last tile (N = 1000): the
+    reference max must move there, and fp16 weights must stay finite."""
+    q, k, v = inputs.random_qkv((1, 3, 1000, d), dtype, seed=13)
+    q[..., -1] = 4.0
+    k[:, :, pos, -1] = 255.0
+    scale = 1 / math.sqrt(d)
+    o, lse = run(q, k, v, scale)
+    ref_o, ref_lse = oracle_full(q, k, v, scale)
+    check(o, lse, ref_o, ref_lse, dtype, f"spike {dtype} d={d} at {pos}")
 
 
 def test_deterministic():
