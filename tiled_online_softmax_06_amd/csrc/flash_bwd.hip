@@ -61,35 +61,36 @@ template <int D> __device__ __forceinline__ constexpr int swz_rt(int r) {
 typedef short s16x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) s16x4* lds_s16x4;
 
-// A operand from a transposed tile: lane (col, half) of column block dt
-// receives, for contraction rows 16 c2 + {0..3, 8..11} + 4 half of a
-// row-major tile (ROWB-byte rows, swizzle f), element 32 dt + col of each
-// row.  lo / hi are this lane's offsets of the two 4-row halves (the swizzle
-// depends on the row index mod 16, so the +8 rows need their own offset).
-struct TrOff { int lo, hi; };
-
+// A operand from a transposed tile (swizzle swz_rt): lane (col, half) of
+// column block dt receives, for contraction rows 16 c2 + {0..3, 8..11} +
+// 4 half of a row-major tile (ROWB-byte rows), element 32 dt + col of each
+// row.  The lane reads two 4-row halves.  With swz_rt, the offset of column
+// block dt is the block-0 offset XOR 64 dt (the swizzle only permutes the
+// chunk bits that dt does not touch), and the +8-row half sits at the
+// 4-row offset XOR 32 (swz_rt(r + 8) = swz_rt(r) ^ 2) plus 8 rows; so one
+// offset per lane, tr_offset0, serves every block and half.
 template <int ROWB>
-__device__ __forceinline__ u32x4 read_tr(const char* tile, int c2row0, TrOff off) {
+__device__ __forceinline__ u32x4 read_tr(const char* tile, int c2row0, int off0, int dt) {
     const char* t = tile + c2row0 * ROWB;
-    const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4)(t + off.lo));
-    const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4)(t + off.hi));
-    const u32x2 l2 = __builtin_bit_cast(u32x2, lo), h2 = __builtin_bit_cast(u32x2, hi);
+    const int lo = off0 ^ (64 * dt);
+    const int hi = (lo ^ 32) + 8 * ROWB;
+    const s16x4 l = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4)(t + lo));
+    const s16x4 h = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4)(t + hi));
+    const u32x2 l2 = __builtin_bit_cast(u32x2, l), h2 = __builtin_bit_cast(u32x2, h);
     return u32x4{l2.x, l2.y, h2.x, h2.y};
 }
 
-// Offsets for column block dt: lane 4t+s of each 16-lane group addresses row
-// t (+4 half, +8 for hi) and the 4-element segment s of the group's 16
-// columns; rows are taken mod 16 for the swizzle (chunks c2 start at
-// multiples of 16 rows).
-template <int D, typename SW>
-__device__ __forceinline__ TrOff tr_offset(int lane, int dt, SW sw) {
+// Block-0 offset: lane 4t+s of each 16-lane group addresses row t (+4 half)
+// and the 4-element segment s of the group's 16 columns; rows are taken mod
+// 16 for the swizzle (chunks c2 start at multiples of 16 rows).
+template <int D>
+__device__ __forceinline__ int tr_offset0(int lane) {
     constexpr int ROWB = 2 * D;
     const int half = lane >> 5;
     const int trt = (lane & 15) >> 2, trs = lane & 3, trg = (lane >> 4) & 1;
     const int r = 4 * half + trt;
-    const int ch = 4 * dt + 2 * trg + (trs >> 1);
-    return TrOff{r * ROWB + 16 * (ch ^ sw(r)) + 8 * (trs & 1),
-                 (r + 8) * ROWB + 16 * (ch ^ sw(r + 8)) + 8 * (trs & 1)};
+    const int ch = 2 * trg + (trs >> 1);
+    return r * ROWB + 16 * (ch ^ swz_rt<D>(r)) + 8 * (trs & 1);
 }
 
 // ---------------------------------------------------------------------------
@@ -200,9 +201,7 @@ flash_bwd_dq(const T* __restrict__ Q, const T* __restrict__ K, const T* __restri
 
     const int kxr = half ^ swz_rt<D>(col);   // K row reads: row col (+32 kt)
     const int vxr = half ^ swz_k<D>(col);    // V row reads
-    TrOff ktr[DT];
-#pragma unroll
-    for (int dt = 0; dt < DT; ++dt) ktr[dt] = tr_offset<D>(lane, dt, [](int r) { return swz_rt<D>(r); });
+    const int ktr = tr_offset0<D>(lane);
 
     f32x16 acc[DT];   // dQ^T (d x queries)
 #pragma unroll
@@ -245,7 +244,7 @@ flash_bwd_dq(const T* __restrict__ Q, const T* __restrict__ K, const T* __restri
         auto read2 = [&](auto step) {
             constexpr int i = decltype(step)::value;
             constexpr int pc = i / DT, dt = i % DT;
-            qring[i % (2 * RQ)] = read_tr<ROWB>(kb, 16 * pc, ktr[dt]);
+            qring[i % (2 * RQ)] = read_tr<ROWB>(kb, 16 * pc, ktr, dt);
         };
         static_for<0, 2 * RQ>([&](auto i) { read2(i); });
         // P^T = exp2(S^T c - LSE log2 e); dS^T = P^T (dP^T - D).  Keys past
@@ -392,19 +391,31 @@ flash_bwd_dkdv(const T* __restrict__ Q, const T* __restrict__ K, const T* __rest
     // One streamed tile: 32 query rows of Q and dO of query head h (swizzle
     // swz_rt: read row-wise and transposed), their LSE (log2 units) and D.
     // Units: wave w moves units w and w + 4 of the Q and dO tiles (QUNITS <= 8
-    // each); wave 0 also copies LSE and D.
-    auto issue_tile = [&](int h, int i0, auto stage) {
+    // each); wave 0 also stores LSE and D, loaded into a register one tile
+    // earlier by load_lv (lanes 0..31: LSE, lanes 32..63: D).
+    auto load_lv = [&](int h, int i0) {
+        float lv = 0.f;
+        if (wave == 0) {
+            int ln;   // opaque lane copy: the per-lane address is not kept (and spilled) across the loop
+            asm volatile("v_mov_b32 %0, %1" : "=v"(ln) : "v"(lane));
+            const int64_t rowi = ((int64_t)b * nh + h) * n + min(i0 + (ln & (BQ - 1)), n - 1);
+            lv = (ln < BQ ? LSE : Dr)[rowi];
+        }
+        return lv;
+    };
+    auto issue_tile = [&](int h, int i0, auto stage, float lv) {
         constexpr int st = decltype(stage)::value;
         char* qd = st ? qs1 : qs0;
         char* od = st ? os1 : os0;
         float* ld = st ? ls1 : ls0;
-        // LSE / D first: the LDS store below then waits only for this load,
-        // not for the tile DMAs issued after it.
-        float lv = 0.f;
-        if (wave == 0) {
-            const int64_t rowi = ((int64_t)b * nh + h) * n + min(i0 + (lane & (BQ - 1)), n - 1);
-            lv = lane < BQ ? LSE[rowi] * 1.4426950408889634f : Dr[rowi];
-        }
+        // Per-lane offsets are recomputed here from an opaque copy of the lane
+        // index: hoisted out of the loop they would be spilled, and reloads
+        // between the DMAs make each DMA wait for the one before it.
+        int ln;
+        asm volatile("v_mov_b32 %0, %1" : "=v"(ln) : "v"(lane));
+        const int lr = ln / CPR, lc = ln % CPR;
+        // LSE / D first: a store after the DMAs would wait for them.
+        if (wave == 0) ld[ln] = ln < BQ ? lv * 1.4426950408889634f : lv;   // 2 BQ == 64 lanes
         const int64_t qbase = ((int64_t)b * nh + h) * n * D;
         const __amdgpu_buffer_rsrc_t qrs =
             __builtin_amdgcn_make_buffer_rsrc((void*)(Q + qbase), (short)0, n * ROWB, 0x00020000);
@@ -414,20 +425,17 @@ flash_bwd_dkdv(const T* __restrict__ Q, const T* __restrict__ K, const T* __rest
         for (int k = 0; k < 2; ++k) {
             const int u = wave + NW * k;
             if (u < QUNITS) {
-                const int r = u * RPU + lrow;
-                const int gofs = min(i0 + r, n - 1) * ROWB + 16 * (lch ^ swz_rt<D>(r));
+                const int r = u * RPU + lr;
+                const int gofs = min(i0 + r, n - 1) * ROWB + 16 * (lc ^ swz_rt<D>(r));
                 dma16(qrs, qd + u * 1024, gofs, 0);
                 dma16(ors, od + u * 1024, gofs, 0);
             }
         }
-        if (wave == 0) ld[lane] = lv;   // 2 BQ == 64 lanes
     };
 
     const int qxr = half ^ swz_rt<D>(col);   // Q / dO row reads: row col
     const int vxr = half ^ swz_k<D>(col);    // V^T B operand: row of this lane's key
-    TrOff qtr[DT];
-#pragma unroll
-    for (int dt = 0; dt < DT; ++dt) qtr[dt] = tr_offset<D>(lane, dt, [](int r) { return swz_rt<D>(r); });
+    const int qtr = tr_offset0<D>(lane);
     const char* vrow = vs + (wave * 32 + col) * ROWB;
 
     f32x16 dka[DT], dva[DT];   // dK^T, dV^T (d x keys)
@@ -444,7 +452,7 @@ flash_bwd_dkdv(const T* __restrict__ Q, const T* __restrict__ K, const T* __rest
     // vector work.
     constexpr int RB = D == 128 ? 2 : 1;
     u32x4 ring[3 * RB];
-    auto compute = [&](auto stage, int i0) {
+    auto compute = [&](auto stage, int i0, auto&& after_reads) {
         constexpr int st = decltype(stage)::value;
         const char* qb = st ? qs1 : qs0;
         const char* ob = st ? os1 : os0;
@@ -470,8 +478,8 @@ flash_bwd_dkdv(const T* __restrict__ Q, const T* __restrict__ K, const T* __rest
         auto read2 = [&](auto step) {
             constexpr int i = decltype(step)::value;
             constexpr int c2 = i / DT, dt = i % DT;
-            ring[2 * (i % RB) + 0] = read_tr<ROWB>(ob, 16 * c2, qtr[dt]);
-            ring[2 * (i % RB) + 1] = read_tr<ROWB>(qb, 16 * c2, qtr[dt]);
+            ring[2 * (i % RB) + 0] = read_tr<ROWB>(ob, 16 * c2, qtr, dt);
+            ring[2 * (i % RB) + 1] = read_tr<ROWB>(qb, 16 * c2, qtr, dt);
         };
         static_for<0, RB>([&](auto i) { read2(i); });
         // P = exp2(S c - LSE log2 e), dS = P (dP - D); register r holds query
@@ -507,6 +515,10 @@ flash_bwd_dkdv(const T* __restrict__ Q, const T* __restrict__ K, const T* __rest
         const u32x4 bp[2] = {M::pack(&p[0]), M::pack(&p[8])};
         const u32x4 bs[2] = {M::pack(&ds[0]), M::pack(&ds[8])};
         // dV^T += dO^T P and dK^T += Q^T dS (contraction over the 32 queries).
+        // The next tile's DMA goes out right after this tile's last LDS read:
+        // the compiler cannot tell that the DMA (into the other stage) and
+        // these reads do not overlap and would make any later read wait for
+        // it; here it overlaps the remaining products instead.
         static_for<0, 2 * DT>([&](auto step) {
             constexpr int i = decltype(step)::value;
             constexpr int c2 = i / DT, dt = i % DT;
@@ -514,6 +526,10 @@ flash_bwd_dkdv(const T* __restrict__ Q, const T* __restrict__ K, const T* __rest
             dva[dt] = M::run(ring[2 * (i % RB) + 0], bp[c2], dva[dt]);
             dka[dt] = M::run(ring[2 * (i % RB) + 1], bs[c2], dka[dt]);
             if constexpr (i + RB < 2 * DT) read2(Int<i + RB>{});
+            if constexpr (i + RB == 2 * DT - 1 || (RB >= 2 * DT && i == 0)) {
+                __builtin_amdgcn_sched_barrier(0);
+                after_reads();
+            }
         });
         __builtin_amdgcn_sched_barrier(0);
     };
@@ -523,17 +539,26 @@ flash_bwd_dkdv(const T* __restrict__ Q, const T* __restrict__ K, const T* __rest
     const int steps = grp * qtiles;
     auto head_of = [&](int t) { return g * grp + t / qtiles; };
     auto row_of = [&](int t) { return (t % qtiles) * BQ; };
-    issue_tile(head_of(0), row_of(0), Int<0>{});
+    // After tile t's last LDS read (see compute): the LSE/D store and the
+    // Q/dO DMA of tile t + 1 (its LSE/D loaded one tile earlier), then the
+    // LSE/D load of tile t + 2.  No global load is in flight while a tile
+    // computes, so waits for spill reloads there wait for nothing else.
+    issue_tile(head_of(0), row_of(0), Int<0>{}, load_lv(head_of(0), row_of(0)));
+    float lv_next = steps > 1 ? load_lv(head_of(1), row_of(1)) : 0.f;
+    auto next = [&](int t, auto stage) {
+        if (t + 1 < steps) {
+            issue_tile(head_of(t + 1), row_of(t + 1), stage, lv_next);
+            if (t + 2 < steps) lv_next = load_lv(head_of(t + 2), row_of(t + 2));
+        }
+    };
     for (int t = 0;;) {
         __builtin_amdgcn_s_waitcnt(0x0070);   // vmcnt(0) lgkmcnt(0): own loads and LDS stores done
         __syncthreads();
-        if (t + 1 < steps) issue_tile(head_of(t + 1), row_of(t + 1), Int<1>{});
-        compute(Int<0>{}, row_of(t));
+        compute(Int<0>{}, row_of(t), [&]() { next(t, Int<1>{}); });
         if (++t == steps) break;
         __builtin_amdgcn_s_waitcnt(0x0070);
         __syncthreads();
-        if (t + 1 < steps) issue_tile(head_of(t + 1), row_of(t + 1), Int<0>{});
-        compute(Int<1>{}, row_of(t));
+        compute(Int<1>{}, row_of(t), [&]() { next(t, Int<0>{}); });
         if (++t == steps) break;
     }
 
