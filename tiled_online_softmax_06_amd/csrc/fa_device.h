@@ -17,8 +17,8 @@ typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
 
 constexpr float kLn2 = 0.693147180559945309f;
-// The reference max is raised only when a tile max exceeds it by more than
-// this (log2 units): weights stay <= 2^8, well inside fp16/bf16/fp32 range.
+// fp32 forward kernel: the reference max is raised only when a tile max
+// exceeds it by more than this (log2 units), so weights stay <= 2^8.
 constexpr float kRescaleSlack = 8.0f;
 // Bound on one lane's sum of a tile's weights before the fp16/bf16 forward
 // kernels raise their reference max: weights stay <= 2^12, inside fp16 range
