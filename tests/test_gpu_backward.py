@@ -89,6 +89,15 @@ def test_backward_grouped_kv_heads(d, H, Hkv):
     full_case(2, H, Hkv, 200, d, "bf16", seed=70 + H + d)
 
 
+@pytest.mark.parametrize("H,Hkv,N", [(1, 1, 32), (1, 1, 33), (3, 1, 32), (4, 2, 33), (2, 1, 97)])
+def test_backward_query_stream_lengths(H, Hkv, N):
+    """The dK/dV kernel streams (query head, 32-row query block) pairs and
+    prefetches the next pair's Q/dO tile and LSE/D one and two steps ahead:
+    one pair, two pairs, a head change on every pair (one block per head),
+    head changes with a ragged last block, and an odd pair count."""
+    full_case(1, H, Hkv, N, 128, "bf16", seed=300 + 10 * H + N)
+
+
 @pytest.mark.parametrize("scale", [0.0, -0.09, 0.6])
 def test_backward_scales(scale):
     full_case(1, 2, 2, 160, 128, "fp16", seed=90, scale=scale)
