@@ -23,10 +23,11 @@
 //     e, bytes 8 s .. 8 s + 7 of an 8-row x 16-byte block; lane 8 s + c then
 //     receives column 8 s + c of the block (byte e from row e).  V^T, the A
 //     operand of O^T += V^T P^T, is read this way: read r (0..3) of lane
-//     (dim, half) covers keys 16 r + 8 half + 0..7.
+//     (dim, half) covers LDS rows 16 r + 8 half + 0..7 of the V tile.
 //   * P leaves the score accumulator in runs of 4 keys (lane half h holds
-//     keys 8 q + 4 h + 0..3); packed to e4m3, one v_permlane32_swap per pair
-//     of dwords regroups them into runs of 8 keys matching those reads.
+//     keys 8 q + 4 h + 0..3) and is packed to e4m3 in that order; the V tile
+//     is stored in LDS with bits 2 and 3 of the key index swapped, so that
+//     the transpose reads return V rows in the same key order.
 #include <hip/hip_runtime.h>
 #include <float.h>
 #include <math.h>
@@ -155,10 +156,14 @@ flash_fwd_fp8(const uint8_t* __restrict__ Q, const uint8_t* __restrict__ K, cons
 #pragma unroll
         for (int i = 0; i < UPW; ++i) {
             const int r = (wave * UPW + i) * RPU + lrow;
+            // V: LDS row r holds key r with bits 2 and 3 swapped, the order
+            // in which P leaves the score accumulators (see the P.V product)
+            const int rv = (r & ~12) | ((r & 4) << 1) | ((r & 8) >> 1);
             // ragged last tile: rows past the end re-read the last row
             const int g = min(j0 + r, n - 1) * ROWB;
+            const int gv = min(j0 + rv, n - 1) * ROWB;
             dma16(krs, kdst + i * 1024, g + 16 * (lch ^ swz8_k<D>(r)), 0);
-            dma16(vrs, vdst + i * 1024, g + 16 * (lch ^ swz8_v<D>(r)), 0);
+            dma16(vrs, vdst + i * 1024, gv + 16 * (lch ^ swz8_v<D>(r)), 0);
         }
     };
 
@@ -252,22 +257,18 @@ flash_fwd_fp8(const uint8_t* __restrict__ Q, const uint8_t* __restrict__ K, cons
             for (int r = 0; r < 16; ++r) part[r & 3] += s[kt][r];
         lsum += (part[0] + part[1]) + (part[2] + part[3]);
 
-        // P^T as the B operand: dword (kt, q) holds keys 32 kt + 8 q + 4 half
-        // + 0..3; swapping the upper half of dword 2p with the lower half of
-        // dword 2p + 1 leaves lane half h with keys 32 kt + 16 p + 8 h + 0..7
-        // in (dword 2p, dword 2p + 1), i.e. read r = 2 kt + p of 64-key
-        // group kt / 2.
+        // P^T as the B operand, straight from the accumulators: dword
+        // w = 4 kt + q of lane half h holds keys 32 kt + 8 q + 4 h + 0..3.
+        // The transpose read r of lane half h returns LDS rows 16 r + 8 h +
+        // 0..7 of its 64-key group as dwords 2 r, 2 r + 1, and the V tile
+        // stores key 16 r + 8 s + 4 h + e at LDS row 16 r + 8 h + 4 s + e,
+        // so both operands pair the same key in every byte.
         int pw[8 * G];
 #pragma unroll
         for (int kt = 0; kt < KT; ++kt)
 #pragma unroll
-            for (int p = 0; p < 2; ++p) {
-                const int x = pack_fp8(s[kt][8 * p + 0], s[kt][8 * p + 1], s[kt][8 * p + 2], s[kt][8 * p + 3]);
-                const int y = pack_fp8(s[kt][8 * p + 4], s[kt][8 * p + 5], s[kt][8 * p + 6], s[kt][8 * p + 7]);
-                const auto sw = __builtin_amdgcn_permlane32_swap((unsigned)x, (unsigned)y, false, false);
-                pw[4 * kt + 2 * p + 0] = (int)sw[0];
-                pw[4 * kt + 2 * p + 1] = (int)sw[1];
-            }
+            for (int q = 0; q < 4; ++q)
+                pw[4 * kt + q] = pack_fp8(s[kt][4 * q + 0], s[kt][4 * q + 1], s[kt][4 * q + 2], s[kt][4 * q + 3]);
         // O^T += V^T P^T: per 64-key group, four transpose reads of 8 keys
         // per operand.
 #pragma unroll
