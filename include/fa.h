@@ -45,7 +45,7 @@ typedef enum {
     FA_ERR_UNSUPPORTED_DTYPE = 4,     /* dtype is not one of fa_dtype_t                 */
     FA_ERR_MISALIGNED = 5,            /* Q/K/V/O not 16-byte or LSE not 4-byte aligned  */
     FA_ERR_ALIAS = 6,                 /* O or LSE overlaps an input or each other       */
-    FA_ERR_BAD_SCALE = 7,             /* scale is NaN or infinite                       */
+    FA_ERR_BAD_SCALE = 7,             /* scale not finite, or |scale|*log2(e) overflows */
     FA_ERR_LAUNCH = 8,                /* the HIP kernel launch itself failed            */
     FA_ERR_WORKSPACE = 9              /* workspace NULL or smaller than required        */
 } fa_status_t;

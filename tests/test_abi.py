@@ -92,6 +92,9 @@ def test_error_codes(lib):
     assert call(lib, dtype=-1) == codes["FA_ERR_UNSUPPORTED_DTYPE"]
     for bad in (math.nan, math.inf, -math.inf):
         assert call(lib, scale=bad) == codes["FA_ERR_BAD_SCALE"]
+    # finite scales whose base-2 factor |scale| log2(e) overflows float32
+    for bad in (3e38, -3e38, 2.4e38):
+        assert call(lib, scale=bad) == codes["FA_ERR_BAD_SCALE"], bad
     for field in ("q", "k", "v", "o", "lse"):
         assert call(lib, **{field: None}) == codes["FA_ERR_NULL_POINTER"], field
     for field in ("q", "k", "v", "o"):
@@ -150,6 +153,7 @@ def test_backward_error_codes(lib):
     assert call_bwd(lib, d=96) == codes["FA_ERR_UNSUPPORTED_HEAD_DIM"]
     for bad in (math.nan, -math.inf):
         assert call_bwd(lib, scale=bad) == codes["FA_ERR_BAD_SCALE"]
+    assert call_bwd(lib, scale=3e38) == codes["FA_ERR_BAD_SCALE"]      # scale log2(e) overflows float32
     for field in ("q", "k", "v", "o", "do", "lse", "dws", "dq", "dk", "dv"):
         assert call_bwd(lib, **{field: None}) == codes["FA_ERR_NULL_POINTER"], field
     for field in ("q", "k", "v", "o", "do", "dq", "dk", "dv"):
@@ -269,6 +273,12 @@ def test_fp8_error_codes(lib):
     for field in ("scale", "dq", "dk", "dv"):
         assert call_fp8(lib, **{field: math.inf}) == codes["FA_ERR_BAD_SCALE"], field
         assert call_fp8(lib, **{field: math.nan}) == codes["FA_ERR_BAD_SCALE"], field
+    # finite factors whose product scale * dq * dk (times log2 e) overflows
+    # float32, though each one alone is fine
+    assert call_fp8(lib, scale=1e30, dq=1e10, dk=1e10) == codes["FA_ERR_BAD_SCALE"]
+    assert call_fp8(lib, scale=-1e30, dq=1e5, dk=3e3) == codes["FA_ERR_BAD_SCALE"]
+    # a product that underflows float32 is a valid (uniform-weight) call
+    assert call_fp8(lib, N=0, scale=1e-30, dq=1e-20, dk=1e-20) == 0
     for field in ("q", "k", "v", "o", "lse"):
         assert call_fp8(lib, **{field: None}) == codes["FA_ERR_NULL_POINTER"], field
     assert call_fp8(lib, k=A + 64 * MB + 8) == codes["FA_ERR_MISALIGNED"]

@@ -31,7 +31,8 @@ int check_forward(const void* Q, const void* K, const void* V, const void* O, co
     if (dtype != FA_DTYPE_FP32 && dtype != FA_DTYPE_FP16 && dtype != FA_DTYPE_BF16)
         return FA_ERR_UNSUPPORTED_DTYPE;
     if (d != 64 && d != 128) return FA_ERR_UNSUPPORTED_HEAD_DIM;
-    if (!isfinite(scale)) return FA_ERR_BAD_SCALE;
+    float c = 0.f;
+    if (!isfinite(scale) || !fa::exp2_factor(scale, &c)) return FA_ERR_BAD_SCALE;
 
     const int64_t esize = dtype == FA_DTYPE_FP32 ? 4 : 2;
     int64_t bh = 0, rows = 0, elems = 0, bytes = 0, bkv = 0, kvrows = 0, kvelems = 0, kvbytes = 0;
@@ -110,6 +111,10 @@ extern "C" int fa_forward_fp8(const void* Q, const void* K, const void* V, void*
     if (d != 64 && d != 128) return FA_ERR_UNSUPPORTED_HEAD_DIM;
     if (!isfinite(scale) || !isfinite(q_descale) || !isfinite(k_descale) || !isfinite(v_descale))
         return FA_ERR_BAD_SCALE;
+    // the kernel multiplies the scores of the codes by scale * q_descale *
+    // k_descale (in log2 units); that factor must itself be a finite float
+    float c = 0.f;
+    if (!fa::exp2_factor((double)scale * (double)q_descale * (double)k_descale, &c)) return FA_ERR_BAD_SCALE;
     const int64_t oesize = out_dtype == FA_DTYPE_FP32 ? 4 : 2;
     int64_t bh = 0, rows = 0, bytes = 0, obytes = 0, bkv = 0, kvrows = 0, kvbytes = 0;
     if (!mul_ok(B, H, &bh) || !mul_ok(bh, N, &rows) || !mul_ok(rows, d, &bytes) || !mul_ok(bytes, oesize, &obytes) ||
@@ -237,7 +242,8 @@ extern "C" int fa_backward(const void* Q, const void* K, const void* V, const vo
     if (B < 0 || H < 0 || N < 0 || d < 0 || Hkv < 0) return FA_ERR_BAD_SHAPE;
     if (dtype != FA_DTYPE_FP16 && dtype != FA_DTYPE_BF16) return FA_ERR_UNSUPPORTED_DTYPE;
     if (d != 64 && d != 128) return FA_ERR_UNSUPPORTED_HEAD_DIM;
-    if (!isfinite(scale)) return FA_ERR_BAD_SCALE;
+    float c = 0.f;
+    if (!isfinite(scale) || !fa::exp2_factor(scale, &c)) return FA_ERR_BAD_SCALE;
 
     const int64_t esize = 2;
     int64_t bh = 0, rows = 0, elems = 0, bytes = 0, bkv = 0, kvrows = 0, kvelems = 0, kvbytes = 0;

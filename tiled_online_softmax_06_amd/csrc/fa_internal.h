@@ -2,10 +2,29 @@
 // (flash_fwd.hip, flash_fwd_fp8.hip, flash_bwd.hip).  Not installed; include/fa.h is the public header.
 #pragma once
 
+#include <float.h>
+#include <math.h>
 #include <stdint.h>
 #include <hip/hip_runtime_api.h>
 
 namespace fa {
+
+// Factor c = |s| log2(e) that turns raw scores into base-2 exponents: the
+// kernels take every weight as exp2(score * c - m).  Computed in double and
+// rounded to float once.  Returns false when c is not a finite float (|s|
+// above FLT_MAX / log2 e: the kernels would form 0 * inf = NaN); a c below
+// FLT_MIN (s = 0 included) is raised to FLT_MIN, where every finite score
+// times c is far below the rounding of exp2 near 0, so all weights are
+// exactly 1 as for a zero factor, while a masked score -inf times c stays
+// -inf (times 0 it would be NaN).
+inline bool exp2_factor(double s, float* c) {
+    const double x = fabs(s) * 1.4426950408889634;
+    if (!(x <= (double)FLT_MAX)) return false;
+    const float f = (float)x;
+    if (!(f <= FLT_MAX)) return false;          // rounded up to infinity
+    *c = f < FLT_MIN ? FLT_MIN : f;
+    return true;
+}
 
 struct FwdArgs {
     const void* q;

@@ -585,7 +585,11 @@ template <typename T, int D>
 hipError_t launch_bwd_t(const BwdArgs& a, hipStream_t stream) {
     const int n = (int)a.n;
     const int nh = (int)a.h, grp = (int)(a.h / a.hkv);
-    const float c = a.scale * 1.4426950408889634f;   // signed: no masking through -inf here
+    // scale log2(e), signed (no masking through -inf here); the caller has
+    // checked that it is a finite float
+    float c = FLT_MIN;
+    exp2_factor(a.scale, &c);
+    if (a.scale < 0.f) c = -c;
     const float scale = a.scale;
     const T* q = (const T*)a.q;
     const T* k = (const T*)a.k;

@@ -866,11 +866,11 @@ hipError_t launch(Kern kern, int nw, int br, const FwdArgs& a, void* out, float*
     const int n = (int)a.n;
     const int qtiles = (int)((a.n + br - 1) / br);
     const int total = (int)(a.bh * splits * qtiles);
-    // c = |scale| log2(e) (a negative scale negates Q instead).  scale = 0 is
-    // passed as the smallest normal float: every score times it is far below
-    // the rounding of exp2 near 0, so the weights are exactly 1 as for c = 0,
-    // while a masked score -inf times it stays -inf (times 0 it would be NaN).
-    const float c = a.scale == 0.f ? FLT_MIN : fabsf(a.scale) * 1.4426950408889634f;
+    // c = |scale| log2(e) (a negative scale negates Q instead); scale = 0 is
+    // passed as the smallest normal float (exp2_factor).  The caller has
+    // checked that c is finite.
+    float c = FLT_MIN;
+    exp2_factor(a.scale, &c);
     const int negate = a.scale < 0.f ? 1 : 0;
     const T* q = (const T*)a.q;
     const T* k = (const T*)a.k;

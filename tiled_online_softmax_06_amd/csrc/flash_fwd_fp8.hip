@@ -326,12 +326,14 @@ hipError_t launch_fp8_t(const Fp8Args& a, hipStream_t stream) {
     const int n = (int)a.n;
     const int qtiles = (int)((a.n + BR - 1) / BR);
     const int total = (int)(a.bh * qtiles);
-    // The scores of the codes carry scale * dq * dk; c = |that| log2(e), a
-    // negative product negates Q, zero is passed as FLT_MIN (see the 16-bit
-    // forward: -inf masked scores stay -inf).
-    const float sc = a.scale * a.q_descale * a.k_descale;
-    const float c = sc == 0.f ? FLT_MIN : fabsf(sc) * 1.4426950408889634f;
-    const int negate = sc < 0.f ? 1 : 0;
+    // The scores of the codes carry scale * dq * dk (formed in double); c =
+    // |that| log2(e) rounded once, a negative product negates Q, zero is
+    // passed as FLT_MIN (exp2_factor: -inf masked scores stay -inf).  The
+    // caller has checked that c is finite.
+    const double sc = (double)a.scale * (double)a.q_descale * (double)a.k_descale;
+    float c = FLT_MIN;
+    exp2_factor(sc, &c);
+    const int negate = sc < 0.0 ? 1 : 0;
     const float vscale = a.v_descale;
     const uint8_t* q = (const uint8_t*)a.q;
     const uint8_t* k = (const uint8_t*)a.k;
