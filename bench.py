@@ -8,7 +8,11 @@ One step = one fa_forward launch over the whole workload (every query row of
 every head) with Q, K, V, O and LSE already resident in HBM.  Prints one JSON
 line: TFLOP/s counted as 4*B*H*N^2*d (non-causal), the kernel's roofline
 against the MFMA peak, and the CPU oracle timed on a bounded sample of the
-same workload on this host's cores.
+same workload on this host's cores.  The oracle's results are compared with
+the GPU's on every row it computed (the long workload: every row of every
+head); "parity" in the JSON line gives the max-abs errors against the bar
+(O 1e-4 fp32 / 2e-2 fp16, bf16; LSE 1e-3), and the process exits with status
+1 after printing the line when they exceed it.
 
 --op backward times one fa_backward call instead (its three kernels, with
 O and LSE from one forward launch made before timing) and counts
@@ -42,6 +46,12 @@ METRIC_FP8 = "attention fwd TFLOP/s (4·B·H·N²·d) fp8 e4m3 inputs at 1 GPU +
 # MI355X published dense matrix peaks (TFLOP/s) and HBM bandwidth (GB/s).
 PEAK_TFLOPS = {"bf16": 2500.0, "fp16": 2500.0, "fp32": 157.3, "fp8_e4m3": 5000.0}
 PEAK_HBM_GBS = 8000.0
+# Parity bar of the forward (max-abs error over every checked element).
+O_TOL = {"fp32": 1e-4, "fp16": 2e-2, "bf16": 2e-2}
+LSE_TOL = 1e-3
+# Oracle worker threads: at most the CPU share that one GPU of the host is
+# given (16 threads), and no more than this process may run on.
+CPU_SHARE = 16
 KERNEL_SOURCE = os.path.join(HERE, "tiled_online_softmax_06_amd", "csrc", "flash_fwd.hip")
 FP8_SOURCE = os.path.join(HERE, "tiled_online_softmax_06_amd", "csrc", "flash_fwd_fp8.hip")
 BWD_SOURCE = os.path.join(HERE, "tiled_online_softmax_06_amd", "csrc", "flash_bwd.hip")
@@ -101,6 +111,18 @@ def device_info(props, peak_spec, fp8):
     return info
 
 
+def oracle_pool():
+    """(workers, cpus available to this process) for the oracle's thread pool."""
+    avail = len(os.sched_getaffinity(0))
+    return max(1, min(CPU_SHARE, avail)), avail
+
+
+def pool_fields(workers: int, avail: int) -> dict:
+    return {"cores": workers, "host_cpus_available": avail, "os_cpu_count": os.cpu_count(),
+            "pool": f"thread pool of {workers} workers (numpy releases the GIL), one BLAS thread each; "
+                    f"capped at {CPU_SHARE}, the CPU share of one GPU on this host"}
+
+
 def cpu_baseline_backward(w, q, k, v, do, heads: int, workers: int):
     """The backward oracle, untuned, on a bounded sample: the first `heads`
     (b, h) heads of the workload (whole heads: every query and key), one head
@@ -131,10 +153,12 @@ def cpu_baseline_backward(w, q, k, v, do, heads: int, workers: int):
             list(ex.map(job, range(heads)))
         dt = time.perf_counter() - t0
     flops = 10 * heads * w.N * w.N * w.d
-    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": min(workers, heads), "kind": "oracle",
-            "sample": f"first {heads} of {w.B * w.H} heads, every query and key "
-                      f"({flops / 1e9:.1f} GFLOP counted as 10*N^2*d per head, float64)",
-            "seconds": round(dt, 3)}
+    out = {"value": flops / dt / 1e12, "unit": "TFLOP/s", "kind": "oracle",
+           "sample": f"first {heads} of {w.B * w.H} heads, every query and key "
+                     f"({flops / 1e9:.1f} GFLOP counted as 10*N^2*d per head, float64)",
+           "seconds": round(dt, 3)}
+    out.update(pool_fields(min(workers, heads), len(os.sched_getaffinity(0))))
+    return out
 
 
 def cpu_baseline_rows(w, q, k, v, workers: int, gpu_out=None):
@@ -159,7 +183,8 @@ def cpu_baseline_rows(w, q, k, v, workers: int, gpu_out=None):
             results = list(ex.map(lambda r: (r, oracle.attention_ref(q64, k64, v64, scale, rows=r)), parts))
         dt = time.perf_counter() - t0
     flops = 4 * rows.size * w.N * w.d
-    out = {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": workers, "kind": "oracle",
+    out = {"value": flops / dt / 1e12, "unit": "TFLOP/s", **pool_fields(workers, len(os.sched_getaffinity(0))),
+           "kind": "oracle",
            "sample": f"{rows.size} seeded query rows of {w.B * w.H * w.N} (default_rng(2005)), each against "
                      f"its head's {w.N} keys ({flops / 1e9:.2f} GFLOP in float64)",
            "seconds": round(dt, 3),
@@ -172,6 +197,7 @@ def cpu_baseline_rows(w, q, k, v, workers: int, gpu_out=None):
             eo = max(eo, float(np.abs(o_gpu[r].double().numpy() - o_ref).max()))
             el = max(el, float(np.abs(lse_gpu[r].double().numpy() - lse_ref).max()))
         out["sample_max_abs_err"] = {"O": eo, "LSE": el}
+        out["rows_compared"] = int(rows.size)
     return out
 
 
@@ -206,7 +232,8 @@ def cpu_baseline(w, q, k, v, heads: int, chunk: int, workers: int, gpu_out=None)
             results = list(ex.map(job, tasks))
         dt = time.perf_counter() - t0
     flops = 4 * heads * w.N * w.N * w.d
-    out = {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": workers, "kind": "oracle",
+    out = {"value": flops / dt / 1e12, "unit": "TFLOP/s", **pool_fields(workers, len(os.sched_getaffinity(0))),
+           "kind": "oracle",
            "sample": f"first {heads} of {w.B * w.H} heads, all {w.N} query rows each "
                      f"({flops / 1e9:.1f} GFLOP in float64; {len(tasks)} row chunks of {chunk})",
            "seconds": round(dt, 3)}
@@ -219,6 +246,24 @@ def cpu_baseline(w, q, k, v, heads: int, chunk: int, workers: int, gpu_out=None)
             eo = max(eo, float(np.abs(o_gpu[rows].double().numpy() - o_ref).max()))
             el = max(el, float(np.abs(lse_gpu[rows].double().numpy() - lse_ref).max()))
         out["sample_max_abs_err"] = {"O": eo, "LSE": el}
+        out["rows_compared"] = heads * w.N
+    return out
+
+
+def parity_verdict(w, base, fixed_bar: bool):
+    """The oracle comparison the CPU-baseline leg made, against the parity
+    bar (max-abs error on O and LSE over every compared element)."""
+    if base is None or "sample_max_abs_err" not in base:
+        return {"checked": False, "note": "no oracle comparison in this run"}
+    err = base["sample_max_abs_err"]
+    out = {"checked": True, "O_max_abs_err": err["O"], "LSE_max_abs_err": err["LSE"],
+           "rows_compared": base.get("rows_compared"), "rows_total": w.B * w.H * w.N}
+    if not fixed_bar:
+        out["note"] = ("FP8 inputs: no fixed bar; tests/test_gpu_fp8.py asserts the derived per-element bar")
+        return out
+    out["O_tol"] = O_TOL[w.dtype]
+    out["LSE_tol"] = LSE_TOL
+    out["pass"] = bool(err["O"] <= O_TOL[w.dtype] and err["LSE"] <= LSE_TOL)
     return out
 
 
@@ -413,22 +458,24 @@ def main():
         result["config"]["splits"] = splits
         result["unsplit"] = {"ms_per_step": round(unsplit_ms, 5),
                              "value": round(flops / (unsplit_ms * 1e-3) / 1e12, 2)}
+    workers, _ = oracle_pool()
     if not args.no_cpu_baseline and (split or fp8):
-        workers = max(1, min(16, len(os.sched_getaffinity(0))))
         result["cpu_baseline"] = cpu_baseline(w, q, k, v, args.cpu_heads, 512, workers,
                                               gpu_out=(o.cpu(), lse.cpu()))
     elif not args.no_cpu_baseline and backward:
-        workers = max(1, min(16, len(os.sched_getaffinity(0))))
         result["cpu_baseline"] = cpu_baseline_backward(w, q, k, v, do, args.cpu_heads or min(8, workers), workers)
     elif not args.no_cpu_baseline and w.sample_rows and not args.seq_len:
-        workers = max(1, min(16, len(os.sched_getaffinity(0))))
         result["cpu_baseline"] = cpu_baseline_rows(w, q, k, v, workers, gpu_out=(o.cpu(), lse.cpu()))
     elif not args.no_cpu_baseline:
-        workers = max(1, min(16, len(os.sched_getaffinity(0))))
         chunk = 512 if w.N >= 4096 else max(64, w.N // 4)
         result["cpu_baseline"] = cpu_baseline(w, q, k, v, args.cpu_heads, chunk, workers,
                                               gpu_out=(o.cpu(), lse.cpu()))
+    if not backward:
+        result["parity"] = parity_verdict(w, result.get("cpu_baseline"), fixed_bar=not fp8)
     print(json.dumps(result), flush=True)
+    if result.get("parity", {}).get("pass") is False:
+        print(f"parity FAILED: {result['parity']}", file=sys.stderr, flush=True)
+        sys.exit(1)
 
 
 if __name__ == "__main__":
