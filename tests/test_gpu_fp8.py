@@ -1,38 +1,28 @@
 """FP8 (OCP e4m3) forward through the C ABI against the float64 oracle on
 the dequantised inputs.
 
-The kernel rounds the weights P to e4m3 (3 mantissa bits) before the
-product with V: a weight in e4m3's normal range moves by at most 2^-4 of
-itself, so the output moves by at most 2^-4 A(|V|), A(|V|) being the
-attention of |V| (the oracle computes it).  The scores come from the e4m3
-matrix instructions, which sum each 64 products to about 2^-12 of the sum
-of their magnitudes (measured on the device); a score error ds moves the
-output by at most ds (A(|V|) + |O|) and the LSE by at most ds.  Bars:
-
-    ds = 2^-12 |scale dq dk| max_i |Q_i| max_j |K_j|     (|.|: Euclidean norm)
-    |O - O_ref|   <= (2^-4 + ds) A(|V|) + (u_out + ds) |O_ref| + 2^-10 max|V|
-    |LSE - LSE_ref| <= ds + 1e-5
-
-with u_out the output type's rounding (2^-8 bf16, 2^-11 fp16, 0 fp32).  The
-last O term covers weights below e4m3's normal range: the kernel keeps the
-row's largest weight at 2^7 or more, so only keys below 2^-13 of the maximum
-are subnormal, each off by at most 2^-10 / 2^7 = 2^-17 of the row sum; that
-is a bound for N <= 128 keys and covers the tails of these input
-distributions beyond.  The equal-keys and one-hot cases pin the operand
-layouts on their own.
+The bar is derived in tests/fp8_bar.py from the kernel's arithmetic: float32
+roundings, the e4m3 rounding of the weights P (2^-4 relative for normal
+weights; 2^-10 absolute for subnormal ones, which the kernel's reference rule
+confines to keys more than 13 binades below the row max, at most 2^-17 of the
+row sum each, for any N), and two stated assumptions: A1, each e4m3 matrix
+instruction sums its 64 exact products to within 2^-11 of the sum of their
+magnitudes before one float32 rounding (the OCP FP8 / microscaling documents
+leave that precision implementation-defined); A2, v_exp_f32 / v_log_f32 within
+2 ulps.  Every element of O and LSE must be within its bar; A1 itself is
+checked on the device by test_fp8_score_model_single_key.
 """
 import numpy as np
 import pytest
 import torch
 
-import oracle
+from fp8_bar import fp8_bars, score_model_bound
 from tiled_online_softmax_06_amd import fa, inputs
 
 pytestmark = pytest.mark.gpu
 
 DEV = "cuda:0"
 OUT = {"bf16": torch.bfloat16, "fp16": torch.float16, "fp32": torch.float32}
-OUT_ULP = {"bf16": 2.0 ** -8, "fp16": 2.0 ** -11, "fp32": 0.0}
 
 
 def f32(x):
@@ -47,24 +37,19 @@ def run_fp8(q8, k8, v8, ds, scale, out="bf16"):
     return o.cpu().to(torch.float64).numpy(), lse.cpu().to(torch.float64).numpy()
 
 
-def bars(qd, kd, vd, scale, out="bf16"):
-    """Oracle output and the O / LSE bars of the module docstring."""
-    ref_o, ref_l = oracle.attention_ref(qd, kd, vd, f32(scale))
-    abs_o, _ = oracle.attention_ref(qd, kd, np.abs(vd), f32(scale))
-    ds = 2.0 ** -12 * abs(f32(scale)) * np.linalg.norm(qd, axis=-1).max() * np.linalg.norm(kd, axis=-1).max()
-    o_bar = (2.0 ** -4 + ds) * abs_o + (OUT_ULP[out] + ds) * np.abs(ref_o) + 2.0 ** -10 * np.abs(vd).max()
-    return ref_o, ref_l, o_bar, ds + 1e-5
-
-
-def check(o, lse, qd, kd, vd, scale, out, what):
-    ref_o, ref_l, o_bar, lse_bar = bars(qd, kd, vd, scale, out)
+def check(o, lse, qd, kd, vd, scale, out, what, rows=None):
+    """Every element (or every element of `rows`) within its derived bar."""
+    ref_o, ref_l, o_bar, lse_bar = fp8_bars(qd, kd, vd, f32(scale), out, rows=rows)
+    if rows is not None:
+        o = o.reshape(-1, o.shape[-1])[rows]
+        lse = lse.reshape(-1)[rows]
     assert np.isfinite(o).all() and np.isfinite(lse).all(), f"{what}: non-finite output"
     ratio = float((np.abs(o - ref_o) / o_bar).max())
-    el = float(np.abs(lse - ref_l).max())
-    print(f"{what}: max|dO| {np.abs(o - ref_o).max():.3e} (worst / bar {ratio:.3f}) max|dLSE| {el:.3e} "
-          f"(bar {lse_bar:.2e})", flush=True)
+    lratio = float((np.abs(lse - ref_l) / lse_bar).max())
+    print(f"{what}: max|dO| {np.abs(o - ref_o).max():.3e} (worst / bar {ratio:.3f}) max|dLSE| "
+          f"{np.abs(lse - ref_l).max():.3e} (worst / bar {lratio:.3f})", flush=True)
     assert ratio <= 1.0, f"{what}: O error above the bar (ratio {ratio:.3f})"
-    assert el <= lse_bar, f"{what}: LSE error {el:.3e} > {lse_bar:.2e}"
+    assert lratio <= 1.0, f"{what}: LSE error above the bar (ratio {lratio:.3f})"
 
 
 def fp8_case(B, H, Hkv, N, d, seed, out="bf16", scale=None, sigma=1.0):
@@ -115,9 +100,9 @@ def test_fp8_descale_signs():
 
 
 def test_fp8_equal_keys_give_mean_v():
-    """All keys equal: every weight is exactly 1 (no e4m3 rounding), so O is
-    the mean of V to float32 summation and bf16 output rounding; this pins
-    the transposed V operand and the key regrouping of P on its own."""
+    """All keys equal: every weight is the same float32 number, so O is the
+    mean of V to float32 summation (here fp32 output); this pins the
+    transposed V operand and the key order of P on its own."""
     N, d = 320, 128
     q8, k8, v8, ds = inputs.random_fp8((1, 2, N, d), 560)
     k8 = k8[:, :, :1].expand(-1, -1, N, -1).contiguous()
@@ -126,10 +111,12 @@ def test_fp8_equal_keys_give_mean_v():
     ref = np.broadcast_to(vd.mean(axis=2, keepdims=True), o.shape)
     err = float(np.abs(o - ref).max())
     print(f"equal keys: max|dO| {err:.3e}", flush=True)
+    # N float32 additions of |v| <= max|V| terms in the P.V accumulator
+    # (A1 per 64-key instruction, 2^-24 per tile) and two roundings of the
+    # normalisation: far below 1e-5 max|V| at N = 320
     assert err <= 1e-5 * np.abs(vd).max()
     qd, kd = inputs.dequantize(q8, ds[0]), inputs.dequantize(k8, ds[1])
-    ref_l = 0.1 * np.einsum("bhnd,bhd->bhn", qd, kd[:, :, 0]) + np.log(N)
-    assert np.abs(lse - ref_l).max() <= bars(qd, kd, vd, 0.1, "fp32")[3]
+    check(o, lse, qd, kd, vd, 0.1, "fp32", "fp8 equal keys")
 
 
 def test_fp8_one_hot_values_read_out_weights():
@@ -154,20 +141,42 @@ def test_fp8_long_workload_sampled_rows():
     lse = torch.empty(q8.shape[:3], dtype=torch.float32, device=DEV)
     fa.forward_fp8_into(q8.to(DEV), k8.to(DEV), v8.to(DEV), ds, o, lse, w.scale)
     torch.cuda.synchronize()
-    o = o.cpu().to(torch.float64).numpy().reshape(-1, w.d)
-    lse = lse.cpu().to(torch.float64).numpy().reshape(-1)
-    assert np.isfinite(o).all() and np.isfinite(lse).all()
+    o = o.cpu().to(torch.float64).numpy()
+    lse = lse.cpu().to(torch.float64).numpy()
     rows = np.union1d(inputs.sample_rows(w, 256), [0, 127, 128, w.N - 1, w.N, w.B * w.H * w.N - 1])
     qd, kd, vd = (inputs.dequantize(c, s) for c, s in zip((q8, k8, v8), ds))
-    ref_o, ref_l = oracle.attention_ref(qd, kd, vd, f32(w.scale), rows=rows)
-    abs_o, _ = oracle.attention_ref(qd, kd, np.abs(vd), f32(w.scale), rows=rows)
-    ds = 2.0 ** -12 * f32(w.scale) * np.linalg.norm(qd, axis=-1).max() * np.linalg.norm(kd, axis=-1).max()
-    o_bar = (2.0 ** -4 + ds) * abs_o + (2.0 ** -8 + ds) * np.abs(ref_o) + 2.0 ** -10 * np.abs(vd).max()
-    ratio = float((np.abs(o[rows] - ref_o) / o_bar).max())
-    lse_bar = ds + 1e-5
-    el = float(np.abs(lse[rows] - ref_l).max())
-    print(f"long fp8: max|dO| {np.abs(o[rows] - ref_o).max():.3e} ratio {ratio:.3f} max|dLSE| {el:.3e}", flush=True)
-    assert ratio <= 1.0 and el <= lse_bar
+    assert np.isfinite(o).all() and np.isfinite(lse).all()
+    check(o, lse, qd, kd, vd, w.scale, "bf16", "long fp8 (sampled rows)", rows=rows)
+
+
+@pytest.mark.parametrize("d", [64, 128])
+def test_fp8_score_model_single_key(d):
+    """Assumption A1 on the device: with one key per head the only weight is
+    the row's, so the kernel's LSE is its score up to the exponential and
+    logarithm.  2048 heads: quantised N(0, 1) draws, heads whose products
+    span many binades (one at e4m3's largest value, the others small) and
+    heads whose large products cancel (a key that is the query negated plus
+    noise)."""
+    B, H = 4, 512
+    q8, k8, v8, ds = inputs.random_fp8((B, H, 1, d), 590 + d)
+    qf = q8.to(torch.float32)
+    kf = k8.to(torch.float32)
+    # heads 128..255: one product near the e4m3 maximum, the others small
+    kf[:, 128:256] *= 2.0 ** -6
+    kf[:, 128:256, :, 0] = 448.0
+    qf[:, 128:256, :, 0] = 448.0
+    # heads 256..383: K close to -Q (large products that cancel)
+    kf[:, 256:384] = -qf[:, 256:384] + kf[:, 256:384] * 2.0 ** -4
+    q8 = qf.to(torch.float8_e4m3fn)
+    k8 = kf.to(torch.float8_e4m3fn)
+    scale = 1.0 / np.sqrt(d)
+    o, lse = run_fp8(q8, k8, v8, ds, scale, "fp32")
+    qd, kd = inputs.dequantize(q8, ds[0]), inputs.dequantize(k8, ds[1])
+    s, bound = score_model_bound(qd, kd, f32(scale))
+    err = np.abs(lse - s)
+    worst = float((err / bound).max())
+    print(f"A1 check d={d}: max|LSE - S| {err.max():.3e}, worst / bound {worst:.3f}", flush=True)
+    assert worst <= 1.0
 
 
 def test_fp8_deterministic():
