@@ -47,8 +47,12 @@ typedef enum {
     FA_ERR_ALIAS = 6,                 /* O or LSE overlaps an input or each other       */
     FA_ERR_BAD_SCALE = 7,             /* scale not finite, or |scale|*log2(e) overflows */
     FA_ERR_LAUNCH = 8,                /* the HIP kernel launch itself failed            */
-    FA_ERR_WORKSPACE = 9              /* workspace NULL or smaller than required        */
+    FA_ERR_WORKSPACE = 9,             /* workspace NULL or smaller than required        */
+    FA_ERR_SCRATCH_LIMIT = 10         /* sizes need more than FA_SCRATCH_BYTES          */
 } fa_status_t;
+
+/* Bytes of the fixed device scratch of fa_forward_split_noalloc (64 MiB). */
+#define FA_SCRATCH_BYTES ((int64_t)64 << 20)
 
 /*
  * fa_forward — attention forward for a batch of heads.
@@ -204,6 +208,27 @@ int fa_forward_split(const void* Q, const void* K, const void* V, void* O, float
                      int64_t B, int64_t H, int64_t H_kv, int64_t N, int64_t d,
                      float scale, int dtype, int64_t splits, void* workspace,
                      int64_t workspace_bytes, hipStream_t stream);
+
+/*
+ * fa_forward_split_noalloc — fa_forward_split with no workspace argument,
+ * for callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc).  It calls
+ * no allocating routine: the partial results go to a fixed device array of
+ * FA_SCRATCH_BYTES inside the library, one per GPU, held until the process
+ * ends (its address is looked up on the first call on each device).
+ *
+ * Arguments, split plan, result, ownership and errors are those of
+ * fa_forward_split, minus workspace / workspace_bytes.  The partials need
+ * fa_split_workspace_bytes(B, H, N, d, splits) bytes; more than
+ * FA_SCRATCH_BYTES returns FA_ERR_SCRATCH_LIMIT before anything is launched
+ * (one range needs none: it runs fa_forward_gqa).  Every call on a GPU shares
+ * that GPU's scratch, so calls that may overlap in time on one GPU (other
+ * streams, other host threads) race and give wrong results: order them on
+ * one stream or use fa_forward_split with a workspace of their own.
+ */
+int fa_forward_split_noalloc(const void* Q, const void* K, const void* V, void* O, float* LSE,
+                             int64_t B, int64_t H, int64_t H_kv, int64_t N, int64_t d,
+                             float scale, int dtype, int64_t splits, hipStream_t stream);
 
 /* Workspace bytes fa_forward_split needs for these sizes and requested
  * splits (0 when one range results or B*H*N == 0; -1 for invalid sizes). */

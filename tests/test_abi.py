@@ -37,8 +37,8 @@ def _header_enum(name):
 def test_exports_every_declared_function(lib):
     funcs = _header_functions()
     assert set(funcs) == {"fa_forward", "fa_forward_gqa", "fa_backward", "fa_forward_split", "fa_forward_fp8",
-                          "fa_split_workspace_bytes", "fa_split_suggest", "fa_merge", "fa_status_string",
-                          "fa_version"}
+                          "fa_forward_split_noalloc", "fa_split_workspace_bytes", "fa_split_suggest", "fa_merge",
+                          "fa_status_string", "fa_version"}
     out = subprocess.run(["nm", "-D", "--defined-only", lib._name], capture_output=True, text=True).stdout
     exported = set(re.findall(r" T (\w+)$", out, flags=re.M))
     for f in funcs:
@@ -232,6 +232,33 @@ def test_split_error_codes(lib):
     assert call_split(lib, o=A + 64) == codes["FA_ERR_ALIAS"]                   # the forward's own checks
     assert call_split(lib, q=None) == codes["FA_ERR_NULL_POINTER"]
     assert call_split(lib, N=0, q=None, k=None, v=None, o=None, lse=None, ws=None) == 0
+
+
+def call_noalloc(lib, q=A, k=A + 64 * MB, v=A + 128 * MB, o=A + 192 * MB, lse=A + 256 * MB, B=1, H=2, Hkv=2,
+                 N=1000, d=64, splits=4, scale=0.125, dtype=2):
+    return lib.fa_forward_split_noalloc(q, k, v, o, lse, B, H, Hkv, N, d, scale, dtype, splits, None)
+
+
+def test_split_noalloc_error_codes(lib):
+    """The no-allocation key split checks its arguments like fa_forward_split
+    and rejects sizes whose partial results exceed its fixed scratch, all
+    before any GPU call."""
+    codes = _header_enum("fa_status_t")
+    _split_lib(lib)
+    assert call_noalloc(lib, splits=0) == codes["FA_ERR_BAD_SHAPE"]
+    assert call_noalloc(lib, Hkv=3) == codes["FA_ERR_BAD_SHAPE"]
+    assert call_noalloc(lib, d=80) == codes["FA_ERR_UNSUPPORTED_HEAD_DIM"]
+    assert call_noalloc(lib, scale=math.nan) == codes["FA_ERR_BAD_SCALE"]
+    assert call_noalloc(lib, q=None) == codes["FA_ERR_NULL_POINTER"]
+    assert call_noalloc(lib, o=A + 64) == codes["FA_ERR_ALIAS"]
+    # 8 heads x 4 ranges x 32768 rows x (128 + 1) floats = 541 MB > 64 MiB
+    big = dict(B=1, H=8, Hkv=8, N=32768, d=128, splits=4, o=A + 1024 * MB, lse=A + 1536 * MB,
+               k=A + 256 * MB, v=A + 512 * MB)
+    assert lib.fa_split_workspace_bytes(1, 8, 32768, 128, 4) > (64 << 20)
+    assert call_noalloc(lib, **big) == codes["FA_ERR_SCRATCH_LIMIT"]
+    # the largest that fits: 2 heads x 2 ranges x 16384 rows x 129 floats = 32.25 MiB
+    assert lib.fa_split_workspace_bytes(1, 2, 16384, 128, 2) <= (64 << 20)
+    assert call_noalloc(lib, N=0, q=None, k=None, v=None, o=None, lse=None) == 0
 
 
 def call_merge(lib, op=A, lp=A + 256 * MB, G=2, S=3, M=100, d=64, o=A + 512 * MB, lse=A + 768 * MB, dtype=2):

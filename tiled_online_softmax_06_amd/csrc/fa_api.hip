@@ -2,6 +2,7 @@
 // dispatch to the gfx950 kernels.  No allocation, copy or synchronisation.
 #include <math.h>
 #include <stdint.h>
+#include <mutex>
 #include <hip/hip_runtime.h>
 
 #include "fa_internal.h"
@@ -82,6 +83,31 @@ bool split_bytes(int64_t bh, int64_t N, int64_t d, int64_t ranges, int64_t* obyt
 }
 
 constexpr int64_t kComputeUnits = 256;   // MI355X
+
+// Scratch for fa_forward_split_noalloc: the key split's float32 partial
+// results in a fixed device array (one copy per GPU, held until the process
+// ends).  Host code uses only the per-device address that
+// hipGetSymbolAddress returns, never the array's name.
+static __device__ __align__(256) char scratch[FA_SCRATCH_BYTES];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// Device address of `scratch` on the current device, looked up once per
+// device (with that device current) and kept.
+int scratch_address(void** out) {
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return FA_ERR_LAUNCH;
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (g_scratch_ptr[dev] == nullptr) {
+        void* p = nullptr;
+        if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || p == nullptr) return FA_ERR_LAUNCH;
+        g_scratch_ptr[dev] = p;
+    }
+    *out = g_scratch_ptr[dev];
+    return FA_OK;
+}
 
 }  // namespace
 
@@ -209,6 +235,32 @@ extern "C" int fa_forward_split(const void* Q, const void* K, const void* V, voi
                ? FA_OK : FA_ERR_LAUNCH;
 }
 
+extern "C" int fa_forward_split_noalloc(const void* Q, const void* K, const void* V, void* O, float* LSE,
+                                        int64_t B, int64_t H, int64_t Hkv, int64_t N, int64_t d,
+                                        float scale, int dtype, int64_t splits, hipStream_t stream) {
+    if (splits < 1) return FA_ERR_BAD_SHAPE;
+    FwdSizes sz;
+    const int st = check_forward(Q, K, V, O, LSE, B, H, Hkv, N, d, scale, dtype, &sz);
+    if (st != FA_OK || sz.empty) return st;
+    int64_t ranges = 0, kchunk = 0, ob = 0, lb = 0;
+    split_plan(N, splits, &ranges, &kchunk);
+    fa::FwdArgs a{Q, K, V, O, LSE, sz.bh, H, Hkv, N, (int)d, dtype, scale};
+    if (ranges == 1) return fa::launch_forward(a, stream) == hipSuccess ? FA_OK : FA_ERR_LAUNCH;
+    if (!split_bytes(sz.bh, N, d, ranges, &ob, &lb)) return FA_ERR_BAD_SHAPE;
+    const int64_t wgs = sz.bh * ranges * ((N + fa::kMinRowsPerWorkgroup - 1) / fa::kMinRowsPerWorkgroup);
+    if (wgs > INT32_MAX) return FA_ERR_BAD_SHAPE;
+    if (ob + lb > FA_SCRATCH_BYTES) return FA_ERR_SCRATCH_LIMIT;
+    void* ws = nullptr;
+    const int sa = scratch_address(&ws);
+    if (sa != FA_OK) return sa;
+    // every partial element the merge reads is written by this call's
+    // forward kernels first, so nothing needs clearing
+    float* o_part = (float*)ws;
+    float* lse_part = (float*)((char*)ws + ob);
+    return fa::launch_forward_split(a, (int)ranges, (int)kchunk, o_part, lse_part, stream) == hipSuccess
+               ? FA_OK : FA_ERR_LAUNCH;
+}
+
 extern "C" int fa_merge(const float* O_parts, const float* LSE_parts, int64_t G, int64_t S, int64_t M,
                         int64_t d, void* O, float* LSE, int dtype, hipStream_t stream) {
     if (G < 0 || S < 0 || M < 0 || d < 0) return FA_ERR_BAD_SHAPE;
@@ -290,6 +342,7 @@ extern "C" const char* fa_status_string(int status) {
         case FA_ERR_BAD_SCALE: return "scale is not finite";
         case FA_ERR_LAUNCH: return "kernel launch failed";
         case FA_ERR_WORKSPACE: return "workspace missing or smaller than required";
+        case FA_ERR_SCRATCH_LIMIT: return "partial results exceed the library's fixed scratch (FA_SCRATCH_BYTES)";
         default: return "unknown status";
     }
 }

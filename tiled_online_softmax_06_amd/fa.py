@@ -42,6 +42,9 @@ def load_library():
         lib.fa_forward_split.argtypes = [ctypes.c_void_p] * 5 + [ctypes.c_int64] * 5 + [
             ctypes.c_float, ctypes.c_int, ctypes.c_int64, ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p]
         lib.fa_forward_split.restype = ctypes.c_int
+        lib.fa_forward_split_noalloc.argtypes = [ctypes.c_void_p] * 5 + [ctypes.c_int64] * 5 + [
+            ctypes.c_float, ctypes.c_int, ctypes.c_int64, ctypes.c_void_p]
+        lib.fa_forward_split_noalloc.restype = ctypes.c_int
         lib.fa_split_workspace_bytes.argtypes = [ctypes.c_int64] * 5
         lib.fa_split_workspace_bytes.restype = ctypes.c_int64
         lib.fa_split_suggest.argtypes = [ctypes.c_int64] * 4 + [ctypes.c_int]
@@ -144,6 +147,26 @@ def forward_split_into(q, k, v, o, lse, workspace, splits: int, scale: float | N
                                   ws_ptr, ws_bytes, handle)
     if rc != 0:
         raise RuntimeError(f"fa_forward_split failed: {status_string(rc)} ({rc})")
+
+
+def forward_split_noalloc_into(q, k, v, o, lse, splits: int, scale: float | None = None, stream=None) -> None:
+    """forward_split_into without a workspace: the partial results go to the
+    library's fixed per-GPU scratch (fa_forward_split_noalloc; nothing is
+    allocated).  Calls that overlap in time on one GPU share that scratch."""
+    lib = load_library()
+    _check_forward(q, k, v, o, lse)
+    if tuple(lse.shape) != tuple(q.shape[:3]):
+        raise ValueError("lse must have shape (B, H, N)")
+    B, H, N, d = q.shape
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    handle = _stream_handle(q, stream)
+    with torch.cuda.device(q.device):
+        rc = lib.fa_forward_split_noalloc(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(),
+                                          B, H, k.shape[1], N, d, float(scale), FA_DTYPE[q.dtype], int(splits),
+                                          handle)
+    if rc != 0:
+        raise RuntimeError(f"fa_forward_split_noalloc failed: {status_string(rc)} ({rc})")
 
 
 def forward_split(q, k, v, splits: int | None = None, scale: float | None = None):
