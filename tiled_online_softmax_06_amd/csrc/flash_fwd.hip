@@ -58,8 +58,14 @@
 namespace fa {
 namespace {
 
-template <typename T, int D, int BC, int NW, bool PART>
-__global__ void __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2)))
+// KS = 2 (few workgroups): 2 NW waves; waves w and w + NW hold the same
+// query rows, group g = w / NW takes the key tiles g, g + 2, g + 4, ... into
+// LDS stages of its own, and at the end group 1 hands its running state
+// (m, l, O~) to group 0 through LDS, which merges the two by the merge of two
+// partial softmaxes (R1) and writes the rows.  Twice the waves per SIMD, each
+// with half the key sweep.
+template <typename T, int D, int BC, int NW, int KS, bool PART>
+__global__ void __launch_bounds__(NW * KS * 64) __attribute__((amdgpu_waves_per_eu(2)))
 flash_fwd_16(const T* __restrict__ Q, const T* __restrict__ K, const T* __restrict__ V,
              void* __restrict__ Out, float* __restrict__ LSE,
              int n, int qtiles, int total, float c, int negate, int nh, int grp, int splits, int kchunk)
@@ -77,15 +83,23 @@ flash_fwd_16(const T* __restrict__ Q, const T* __restrict__ K, const T* __restri
     constexpr int KC = D / 16;               // contraction chunks of Q.K^T
     static_assert(UNITS % NW == 0 && BC % 32 == 0, "tile shape");
 
-    // Separate objects per stage and operand, so the compiler can see that the
-    // DMA into one stage never aliases the reads of the other.
+    static_assert(KS == 1 || KS == 2, "key groups");
+    constexpr int TILEB2 = KS > 1 ? TILEB : 16;
+
+    // Separate objects per stage, operand and key group, so the compiler can
+    // see that the DMA into one stage never aliases the reads of another.
     __shared__ __attribute__((aligned(1024))) char ks0[TILEB];
     __shared__ __attribute__((aligned(1024))) char vs0[TILEB];
     __shared__ __attribute__((aligned(1024))) char ks1[TILEB];
     __shared__ __attribute__((aligned(1024))) char vs1[TILEB];
+    __shared__ __attribute__((aligned(1024))) char ks2[TILEB2];
+    __shared__ __attribute__((aligned(1024))) char vs2[TILEB2];
+    __shared__ __attribute__((aligned(1024))) char ks3[TILEB2];
+    __shared__ __attribute__((aligned(1024))) char vs3[TILEB2];
 
     const int lane = threadIdx.x & 63;
-    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int wave = __builtin_amdgcn_readfirstlane((threadIdx.x >> 6) % NW);   // row block
+    const int kgrp = __builtin_amdgcn_readfirstlane((threadIdx.x >> 6) / NW);   // key group
     const int col = lane & 31;
     const int half = lane >> 5;
 
@@ -132,10 +146,18 @@ flash_fwd_16(const T* __restrict__ Q, const T* __restrict__ K, const T* __restri
         vvo[i] = r * ROWB + 16 * (lch ^ swz_v<D>(r));
     }
 
-    auto issue_loads = [&](int j0, auto stage) {
-        constexpr int st = decltype(stage)::value;
-        char* kdst = (st ? ks1 : ks0) + wave * UPW * 1024;
-        char* vdst = (st ? vs1 : vs0) + wave * UPW * 1024;
+    // LDS stages of key group G (compile time): stage 0 / 1 of K and V.
+    auto kst = [&](auto G, auto stage) -> char* {
+        constexpr int g = decltype(G)::value, st = decltype(stage)::value;
+        return g ? (st ? ks3 : ks2) : (st ? ks1 : ks0);
+    };
+    auto vst = [&](auto G, auto stage) -> char* {
+        constexpr int g = decltype(G)::value, st = decltype(stage)::value;
+        return g ? (st ? vs3 : vs2) : (st ? vs1 : vs0);
+    };
+    auto issue_loads = [&](int j0, auto G, auto stage) {
+        char* kdst = kst(G, stage) + wave * UPW * 1024;
+        char* vdst = vst(G, stage) + wave * UPW * 1024;
         if (j0 + BC <= nk) {
 #pragma unroll
             for (int i = 0; i < UPW; ++i) {
@@ -184,10 +206,9 @@ flash_fwd_16(const T* __restrict__ Q, const T* __restrict__ K, const T* __restri
     u32x4 ring[R16];
     typedef short s16x4 __attribute__((ext_vector_type(4)));
     typedef __attribute__((address_space(3))) s16x4* lds_s16x4;
-    auto compute = [&](auto stage, int j0) {
-        constexpr int st = decltype(stage)::value;
-        const char* kb = st ? ks1 : ks0;
-        const char* vb = st ? vs1 : vs0;
+    auto compute = [&](auto G, auto stage, int j0, bool first) {
+        const char* kb = kst(G, stage);
+        const char* vb = vst(G, stage);
         constexpr int N1 = KT * KC;
         constexpr int N2 = KT * 2 * DT;
         auto read1 = [&](auto step) {
@@ -266,7 +287,7 @@ flash_fwd_16(const T* __restrict__ Q, const T* __restrict__ K, const T* __restri
             }
             return (part[0] + part[1]) + (part[2] + part[3]);
         };
-        if (j0 == 0) raise(true);
+        if (first) raise(true);
         float t = weights();
         if (__ballot(t > kTileSumLimit)) {
             raise(false);
@@ -283,20 +304,71 @@ flash_fwd_16(const T* __restrict__ Q, const T* __restrict__ K, const T* __restri
         __builtin_amdgcn_sched_barrier(0);
     };
 
-    // Two LDS stages: while one is computed on, the DMA fills the other.
+    // Two LDS stages per key group: while one is computed on, the DMA fills
+    // the other.  Key group g visits tiles g, g + KS, ...; both groups run the
+    // same number of steps (one barrier each), group 1 idling in the last
+    // step when the tile count is odd.
     const int ntiles = (nk + BC - 1) / BC;
-    issue_loads(0, Int<0>{});
-    for (int t = 0;;) {
-        __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0): this wave's DMA landed
-        __syncthreads();                      // ... every wave's; stage 1 is free
-        if (t + 1 < ntiles) issue_loads((t + 1) * BC, Int<1>{});
-        compute(Int<0>{}, t * BC);
-        if (++t == ntiles) break;
+    const int nsteps = (ntiles + KS - 1) / KS;
+    auto sweep = [&](auto G) {
+        constexpr int g = decltype(G)::value;
+        auto has = [&](int i) { return KS * i + g < ntiles; };
+        if (has(0)) issue_loads(g * BC, G, Int<0>{});
+        for (int i = 0;;) {
+            __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0): this wave's DMA landed
+            __syncthreads();                      // ... every wave's; stage 1 is free
+            if (has(i + 1)) issue_loads((KS * (i + 1) + g) * BC, G, Int<1>{});
+            if (has(i)) compute(G, Int<0>{}, (KS * i + g) * BC, i == 0);
+            if (++i == nsteps) break;
+            __builtin_amdgcn_s_waitcnt(0x0F70);
+            __syncthreads();
+            if (has(i + 1)) issue_loads((KS * (i + 1) + g) * BC, G, Int<0>{});
+            if (has(i)) compute(G, Int<1>{}, (KS * i + g) * BC, false);
+            if (++i == nsteps) break;
+        }
+    };
+    if constexpr (KS == 1) {
+        sweep(Int<0>{});
+    } else {
+        if (kgrp == 0) sweep(Int<0>{});
+        else sweep(Int<1>{});
+    }
+
+    if constexpr (KS > 1) {
+        // Group 1 leaves (m, l, O~) in LDS (lane-major, conflict free); group 0
+        // merges: m = max(m0, m1), l = a0 l0 + a1 l1, O~ = a0 O~0 + a1 O~1 with
+        // a_g = exp2(m_g - m) (a group without keys has m = -inf, a = 0).
         __builtin_amdgcn_s_waitcnt(0x0F70);
+        __syncthreads();                          // every wave is done with the tiles
+        char* accb = wave == 0 ? ks0 : wave == 1 ? vs0 : wave == 2 ? ks1 : vs1;
+        float* ml = (float*)(ks2 + wave * 512);
+        if (kgrp == 1) {
+#pragma unroll
+            for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+                for (int q = 0; q < 4; ++q)
+                    *(float4*)(accb + ((dt * 4 + q) * 64 + lane) * 16) =
+                        make_float4(acc[dt][4 * q], acc[dt][4 * q + 1], acc[dt][4 * q + 2], acc[dt][4 * q + 3]);
+            ml[lane] = mref;
+            ml[64 + lane] = lsum;
+        }
         __syncthreads();
-        if (t + 1 < ntiles) issue_loads((t + 1) * BC, Int<0>{});
-        compute(Int<1>{}, t * BC);
-        if (++t == ntiles) break;
+        if (kgrp == 1) return;
+        const float m1 = ml[lane], l1 = ml[64 + lane];
+        const float mm = fmaxf(mref, m1);
+        const float a0 = __builtin_amdgcn_exp2f(mref - mm), a1 = __builtin_amdgcn_exp2f(m1 - mm);
+        lsum = a0 * lsum + a1 * l1;
+        mref = mm;
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const float4 o1 = *(const float4*)(accb + ((dt * 4 + q) * 64 + lane) * 16);
+                acc[dt][4 * q + 0] = a0 * acc[dt][4 * q + 0] + a1 * o1.x;
+                acc[dt][4 * q + 1] = a0 * acc[dt][4 * q + 1] + a1 * o1.y;
+                acc[dt][4 * q + 2] = a0 * acc[dt][4 * q + 2] + a1 * o1.z;
+                acc[dt][4 * q + 3] = a0 * acc[dt][4 * q + 3] + a1 * o1.w;
+            }
     }
 
     const float ltot = pair_sum(lsum);
@@ -860,6 +932,8 @@ flash_fwd_32(const float* __restrict__ Q, const float* __restrict__ K, const flo
     }
 }
 
+constexpr int64_t kComputeUnitsFwd = 256;   // MI355X
+
 template <typename Kern, typename T>
 hipError_t launch(Kern kern, int nw, int br, const FwdArgs& a, void* out, float* lse, int splits, int kchunk,
                   hipStream_t stream) {
@@ -881,6 +955,24 @@ hipError_t launch(Kern kern, int nw, int br, const FwdArgs& a, void* out, float*
     return hipLaunchKernel((const void*)kern, dim3(total), dim3(nw * 64), args, 0, stream);
 }
 
+// d = 64, fp16/bf16: when the grid holds at most one workgroup per CU (the
+// ragged workload: 256), the key-group variant doubles the waves per SIMD and
+// halves each wave's key sweep.  With more (the GPT-2-shaped workload: 768)
+// the plain kernel keeps three workgroups per CU, where the key-group one (8
+// waves, one workgroup per CU) would need more rounds.
+template <typename T, bool PART>
+hipError_t launch_d64(const FwdArgs& a, void* out, float* lse, int splits, int kchunk, hipStream_t stream) {
+    constexpr int NW = 4;
+    constexpr int BR = 32 * NW;
+    const int64_t wgs = a.bh * splits * ((a.n + BR - 1) / BR);
+    const int64_t keys = splits > 1 ? kchunk : a.n;
+    if (wgs <= kComputeUnitsFwd && keys > 64)
+        return launch<decltype(&flash_fwd_16<T, 64, 64, NW, 2, PART>), T>(
+            &flash_fwd_16<T, 64, 64, NW, 2, PART>, 2 * NW, BR, a, out, lse, splits, kchunk, stream);
+    return launch<decltype(&flash_fwd_16<T, 64, 64, NW, 1, PART>), T>(
+        &flash_fwd_16<T, 64, 64, NW, 1, PART>, NW, BR, a, out, lse, splits, kchunk, stream);
+}
+
 // One launch of the kernel for (dtype, d); PART: fp32 partial outputs.
 template <bool PART>
 hipError_t launch_kernel(const FwdArgs& a, void* out, float* lse, int splits, int kchunk, hipStream_t stream) {
@@ -890,15 +982,11 @@ hipError_t launch_kernel(const FwdArgs& a, void* out, float* lse, int splits, in
         case FA_DTYPE_BF16:
             return a.d == 128 ? launch<decltype(&flash_fwd_pp<__bf16, 128, PART>), __bf16>(
                                     &flash_fwd_pp<__bf16, 128, PART>, 8, 256, a, out, lse, splits, kchunk, stream)
-                              : launch<decltype(&flash_fwd_16<__bf16, 64, 64, NW, PART>), __bf16>(
-                                    &flash_fwd_16<__bf16, 64, 64, NW, PART>, NW, BR, a, out, lse, splits, kchunk,
-                                    stream);
+                              : launch_d64<__bf16, PART>(a, out, lse, splits, kchunk, stream);
         case FA_DTYPE_FP16:
             return a.d == 128 ? launch<decltype(&flash_fwd_pp<_Float16, 128, PART>), _Float16>(
                                     &flash_fwd_pp<_Float16, 128, PART>, 8, 256, a, out, lse, splits, kchunk, stream)
-                              : launch<decltype(&flash_fwd_16<_Float16, 64, 64, NW, PART>), _Float16>(
-                                    &flash_fwd_16<_Float16, 64, 64, NW, PART>, NW, BR, a, out, lse, splits, kchunk,
-                                    stream);
+                              : launch_d64<_Float16, PART>(a, out, lse, splits, kchunk, stream);
         case FA_DTYPE_FP32:
             return a.d == 128 ? launch<decltype(&flash_fwd_32<128, 32, NW, PART>), float>(
                                     &flash_fwd_32<128, 32, NW, PART>, NW, BR, a, out, lse, splits, kchunk, stream)
