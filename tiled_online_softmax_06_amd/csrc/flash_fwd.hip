@@ -580,7 +580,23 @@ flash_fwd_pp(const T* __restrict__ Q, const T* __restrict__ K, const T* __restri
             __builtin_amdgcn_sched_barrier(0);
             mma(i);
             if constexpr (k + R < NS) read(Int<k + R>{});
+            // With both kinds of products in the phase, the tile's exponent
+            // arguments x = s c - m (the same m as the coming softmax phase)
+            // are formed here, two or three per P.V product from the third
+            // on, by the MFMA-phase wave, whose vector issue is otherwise idle.
+            if constexpr (NQK > 0 && NPV > 0 && k >= NQK + 2) {
+                constexpr int kk = k - NQK - 2;
+                constexpr int f0 = (KT * 16) * kk / (NPV - 2), f1 = (KT * 16) * (kk + 1) / (NPV - 2);
+                static_for<f0, f1>([&](auto ff) {
+                    constexpr int q = decltype(ff)::value;
+                    s[q >> 4][q & 15] = fmaf(s[q >> 4][q & 15], c, -mref);
+                });
+            }
         });
+        if constexpr (NQK > 0 && NPV > 0) {
+            // keep the exponent arguments in this phase
+            asm volatile("" : "+v"(s[0]), "+v"(s[1]));
+        }
         __builtin_amdgcn_sched_barrier(0);
         __builtin_amdgcn_s_setprio(0);
         __builtin_amdgcn_sched_barrier(0);
@@ -618,6 +634,8 @@ flash_fwd_pp(const T* __restrict__ Q, const T* __restrict__ K, const T* __restri
         // Raise the reference max to this tile's max (both lanes of a query
         // pair agree) and rescale the running sum and output by
         // exp2(m_old - m_new).
+        // first: s holds raw scores; otherwise x = s c - m from the MFMA phase
+        constexpr bool XF = !decltype(first)::value;
         auto raise = [&](auto first) {
             float mp[4];
 #pragma unroll
@@ -629,13 +647,21 @@ flash_fwd_pp(const T* __restrict__ Q, const T* __restrict__ K, const T* __restri
                     const int q = 2 * kt + (r >> 3);
                     if ((r & 7) >= 2) mp[q] = fmaxf(mp[q], s[kt][r]);
                 }
-            const float mt = pair_max(fmaxf(fmaxf(mp[0], mp[1]), fmaxf(mp[2], mp[3]))) * c;
+            const float mx = pair_max(fmaxf(fmaxf(mp[0], mp[1]), fmaxf(mp[2], mp[3])));
+            const float mt = XF ? mx + mref : mx * c;
             const float mnew = fmaxf(mref, mt);
             if constexpr (!decltype(first)::value) {
                 const float alpha = __builtin_amdgcn_exp2f(mref - mnew);
                 lsum *= alpha;
 #pragma unroll
                 for (int dt = 0; dt < DT; ++dt) acc[dt] *= alpha;
+            }
+            if constexpr (XF) {
+                const float dm = mref - mnew;
+#pragma unroll
+                for (int kt = 0; kt < KT; ++kt)
+#pragma unroll
+                    for (int r = 0; r < 16; ++r) s[kt][r] += dm;
             }
             mref = mnew;
         };
@@ -648,7 +674,8 @@ flash_fwd_pp(const T* __restrict__ Q, const T* __restrict__ K, const T* __restri
                 float w[8];
 #pragma unroll
                 for (int e = 0; e < 8; ++e) {
-                    w[e] = __builtin_amdgcn_exp2f(fmaf(s[pc >> 1][8 * (pc & 1) + e], c, -mref));
+                    w[e] = XF ? __builtin_amdgcn_exp2f(s[pc >> 1][8 * (pc & 1) + e])
+                              : __builtin_amdgcn_exp2f(fmaf(s[pc >> 1][8 * (pc & 1) + e], c, -mref));
                     part[e & 3] = (pc == 0 && e < 4) ? w[e] : part[e & 3] + w[e];
                 }
                 p[pc] = M::pack(w);
