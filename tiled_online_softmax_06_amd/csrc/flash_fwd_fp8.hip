@@ -54,8 +54,13 @@ __device__ __forceinline__ f32x16 mfma_fp8(i32x8 a, i32x8 b, f32x16 c) {
 }
 
 // Four floats to four e4m3 bytes (round to nearest even), byte e = x[e].
+// The first conversion writes the low half of a register whose high half the
+// second one overwrites, so it starts from whatever the register holds (an
+// empty asm statement defines it) rather than from a zeroed register.
 __device__ __forceinline__ int pack_fp8(float x0, float x1, float x2, float x3) {
-    int w = __builtin_amdgcn_cvt_pk_fp8_f32(x0, x1, 0, false);
+    int any;
+    asm volatile("" : "=v"(any));
+    int w = __builtin_amdgcn_cvt_pk_fp8_f32(x0, x1, any, false);
     return __builtin_amdgcn_cvt_pk_fp8_f32(x2, x3, w, true);
 }
 
@@ -149,21 +154,38 @@ flash_fwd_fp8(const uint8_t* __restrict__ Q, const uint8_t* __restrict__ K, cons
 
     const int lrow = lane / CPR;
     const int lch = lane % CPR;
+    // Per-lane DMA offsets within a tile: LDS row r of unit i is key r of
+    // the K tile and key rv of the V tile (r with bits 2 and 3 swapped, the
+    // order in which P leaves the score accumulators; see the P.V product),
+    // at its swizzled chunk.  A full tile adds its byte offset as the scalar
+    // offset; the ragged last tile clamps its keys to the last row.
+    int kdo[UPW], vdo[UPW];
+#pragma unroll
+    for (int i = 0; i < UPW; ++i) {
+        const int r = (wave * UPW + i) * RPU + lrow;
+        const int rv = (r & ~12) | ((r & 4) << 1) | ((r & 8) >> 1);
+        kdo[i] = r * ROWB + 16 * (lch ^ swz8_k<D>(r));
+        vdo[i] = rv * ROWB + 16 * (lch ^ swz8_v<D>(r));
+    }
     auto issue_loads = [&](int j0, auto stage) {
         constexpr int st = decltype(stage)::value;
         char* kdst = (st ? ks1 : ks0) + wave * UPW * 1024;
         char* vdst = (st ? vs1 : vs0) + wave * UPW * 1024;
+        if (j0 + BC <= n) {
+            const int so = __builtin_amdgcn_readfirstlane(j0 * ROWB);
 #pragma unroll
-        for (int i = 0; i < UPW; ++i) {
-            const int r = (wave * UPW + i) * RPU + lrow;
-            // V: LDS row r holds key r with bits 2 and 3 swapped, the order
-            // in which P leaves the score accumulators (see the P.V product)
-            const int rv = (r & ~12) | ((r & 4) << 1) | ((r & 8) >> 1);
-            // ragged last tile: rows past the end re-read the last row
-            const int g = min(j0 + r, n - 1) * ROWB;
-            const int gv = min(j0 + rv, n - 1) * ROWB;
-            dma16(krs, kdst + i * 1024, g + 16 * (lch ^ swz8_k<D>(r)), 0);
-            dma16(vrs, vdst + i * 1024, gv + 16 * (lch ^ swz8_v<D>(r)), 0);
+            for (int i = 0; i < UPW; ++i) {
+                dma16(krs, kdst + i * 1024, kdo[i], so);
+                dma16(vrs, vdst + i * 1024, vdo[i], so);
+            }
+        } else {
+#pragma unroll
+            for (int i = 0; i < UPW; ++i) {
+                const int r = (wave * UPW + i) * RPU + lrow;
+                const int rv = (r & ~12) | ((r & 4) << 1) | ((r & 8) >> 1);
+                dma16(krs, kdst + i * 1024, min(j0 + r, n - 1) * ROWB + 16 * (lch ^ swz8_k<D>(r)), 0);
+                dma16(vrs, vdst + i * 1024, min(j0 + rv, n - 1) * ROWB + 16 * (lch ^ swz8_v<D>(r)), 0);
+            }
         }
     };
 
@@ -250,11 +272,11 @@ flash_fwd_fp8(const uint8_t* __restrict__ Q, const uint8_t* __restrict__ K, cons
         for (int kt = 0; kt < KT; ++kt)
 #pragma unroll
             for (int r = 0; r < 16; ++r) s[kt][r] = __builtin_amdgcn_exp2f(fmaf(s[kt][r], c, -mref));
-        float part[4] = {0.f, 0.f, 0.f, 0.f};
+        float part[4] = {s[0][0], s[0][1], s[0][2], s[0][3]};
 #pragma unroll
         for (int kt = 0; kt < KT; ++kt)
 #pragma unroll
-            for (int r = 0; r < 16; ++r) part[r & 3] += s[kt][r];
+            for (int r = kt ? 0 : 4; r < 16; ++r) part[r & 3] += s[kt][r];
         lsum += (part[0] + part[1]) + (part[2] + part[3]);
 
         // P^T as the B operand, straight from the accumulators: dword
