@@ -199,8 +199,12 @@ flash_bwd_dq(const T* __restrict__ Q, const T* __restrict__ K, const T* __restri
         }
     };
 
-    const int kxr = half ^ swz_rt<D>(col);   // K row reads: row col (+32 kt)
-    const int vxr = half ^ swz_k<D>(col);    // V row reads
+    // LDS read offsets (as in the dK/dV kernel): row reads of step (kt, kc)
+    // at row 32 kt + col, chunk 2 kc + half under the row's swizzle, i.e. the
+    // kc = 0 offset XOR 32 kc; transpose reads from tr_offset0.  Made opaque
+    // once per tile so that the per-step offsets are not kept across the loop.
+    const int koff = col * ROWB + 16 * (half ^ swz_rt<D>(col));
+    const int voff = col * ROWB + 16 * (half ^ swz_k<D>(col));
     const int ktr = tr_offset0<D>(lane);
 
     f32x16 acc[DT];   // dQ^T (d x queries)
@@ -219,12 +223,14 @@ flash_bwd_dq(const T* __restrict__ Q, const T* __restrict__ K, const T* __restri
         constexpr int st = decltype(stage)::value;
         const char* kb = st ? ks1 : ks0;
         const char* vb = st ? vs1 : vs0;
+        int ko = koff, vo = voff, to = ktr;
+        asm volatile("" : "+v"(ko), "+v"(vo), "+v"(to));
         constexpr int N1 = KT * KC;
         auto read1 = [&](auto step) {
             constexpr int i = decltype(step)::value;
             constexpr int kt = i / KC, kc = i % KC;
-            qring[2 * (i % RQ) + 0] = *(const u32x4*)(kb + (32 * kt + col) * ROWB + 16 * ((2 * kc) ^ kxr));
-            qring[2 * (i % RQ) + 1] = *(const u32x4*)(vb + (32 * kt + col) * ROWB + 16 * ((2 * kc) ^ vxr));
+            qring[2 * (i % RQ) + 0] = *(const u32x4*)(kb + 32 * kt * ROWB + (ko ^ (32 * kc)));
+            qring[2 * (i % RQ) + 1] = *(const u32x4*)(vb + 32 * kt * ROWB + (vo ^ (32 * kc)));
         };
         // S^T = K Q^T and dP^T = V dO^T (keys x queries).
         f32x16 s[KT], dp[KT];
@@ -244,7 +250,7 @@ flash_bwd_dq(const T* __restrict__ Q, const T* __restrict__ K, const T* __restri
         auto read2 = [&](auto step) {
             constexpr int i = decltype(step)::value;
             constexpr int pc = i / DT, dt = i % DT;
-            qring[i % (2 * RQ)] = read_tr<ROWB>(kb, 16 * pc, ktr, dt);
+            qring[i % (2 * RQ)] = read_tr<ROWB>(kb, 16 * pc, to, dt);
         };
         static_for<0, 2 * RQ>([&](auto i) { read2(i); });
         // P^T = exp2(S^T c - LSE log2 e); dS^T = P^T (dP^T - D).  Keys past
@@ -433,10 +439,15 @@ flash_bwd_dkdv(const T* __restrict__ Q, const T* __restrict__ K, const T* __rest
         }
     };
 
-    const int qxr = half ^ swz_rt<D>(col);   // Q / dO row reads: row col
-    const int vxr = half ^ swz_k<D>(col);    // V^T B operand: row of this lane's key
+    // LDS read offsets.  Row reads of step kc: row col (Q, dO) or this lane's
+    // key (V), chunk 2 kc + half under the row's swizzle; since rows are
+    // ROWB >= 128 bytes, the offset is the kc = 0 offset XOR 32 kc.  Transpose
+    // reads: tr_offset0 (see read_tr).  The three offsets are made opaque once
+    // per tile (see compute): hoisted, the compiler keeps one register per
+    // (step, operand) offset across the loop and spills at d = 128.
+    const int qoff = col * ROWB + 16 * (half ^ swz_rt<D>(col));
+    const int voff = (wave * 32 + col) * ROWB + 16 * (half ^ swz_k<D>(col));
     const int qtr = tr_offset0<D>(lane);
-    const char* vrow = vs + (wave * 32 + col) * ROWB;
 
     f32x16 dka[DT], dva[DT];   // dK^T, dV^T (d x keys)
 #pragma unroll
@@ -457,11 +468,13 @@ flash_bwd_dkdv(const T* __restrict__ Q, const T* __restrict__ K, const T* __rest
         const char* qb = st ? qs1 : qs0;
         const char* ob = st ? os1 : os0;
         const float* lb = st ? ls1 : ls0;
+        int qo = qoff, vo = voff, to = qtr;
+        asm volatile("" : "+v"(qo), "+v"(vo), "+v"(to));
         auto read1 = [&](auto step) {
             constexpr int kc = decltype(step)::value;
-            ring[3 * (kc % RB) + 0] = *(const u32x4*)(qb + col * ROWB + 16 * ((2 * kc) ^ qxr));
-            ring[3 * (kc % RB) + 1] = *(const u32x4*)(ob + col * ROWB + 16 * ((2 * kc) ^ qxr));
-            ring[3 * (kc % RB) + 2] = *(const u32x4*)(vrow + 16 * ((2 * kc) ^ vxr));
+            ring[3 * (kc % RB) + 0] = *(const u32x4*)(qb + (qo ^ (32 * kc)));
+            ring[3 * (kc % RB) + 1] = *(const u32x4*)(ob + (qo ^ (32 * kc)));
+            ring[3 * (kc % RB) + 2] = *(const u32x4*)(vs + (vo ^ (32 * kc)));
         };
         // S = Q K^T and dP = dO V^T (queries x keys).
         f32x16 s = f32x16(0.f), dp = f32x16(0.f);
@@ -478,8 +491,8 @@ flash_bwd_dkdv(const T* __restrict__ Q, const T* __restrict__ K, const T* __rest
         auto read2 = [&](auto step) {
             constexpr int i = decltype(step)::value;
             constexpr int c2 = i / DT, dt = i % DT;
-            ring[2 * (i % RB) + 0] = read_tr<ROWB>(ob, 16 * c2, qtr, dt);
-            ring[2 * (i % RB) + 1] = read_tr<ROWB>(qb, 16 * c2, qtr, dt);
+            ring[2 * (i % RB) + 0] = read_tr<ROWB>(ob, 16 * c2, to, dt);
+            ring[2 * (i % RB) + 1] = read_tr<ROWB>(qb, 16 * c2, to, dt);
         };
         static_for<0, RB>([&](auto i) { read2(i); });
         // P = exp2(S c - LSE log2 e), dS = P (dP - D); register r holds query
