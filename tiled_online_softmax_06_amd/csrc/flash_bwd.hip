@@ -463,7 +463,7 @@ flash_bwd_dkdv(const T* __restrict__ Q, const T* __restrict__ K, const T* __rest
     // vector work.
     constexpr int RB = D == 128 ? 2 : 1;
     u32x4 ring[3 * RB];
-    auto compute = [&](auto stage, int i0, auto&& after_reads) {
+    auto compute = [&](auto stage, int i0) {
         constexpr int st = decltype(stage)::value;
         const char* qb = st ? qs1 : qs0;
         const char* ob = st ? os1 : os0;
@@ -528,10 +528,6 @@ flash_bwd_dkdv(const T* __restrict__ Q, const T* __restrict__ K, const T* __rest
         const u32x4 bp[2] = {M::pack(&p[0]), M::pack(&p[8])};
         const u32x4 bs[2] = {M::pack(&ds[0]), M::pack(&ds[8])};
         // dV^T += dO^T P and dK^T += Q^T dS (contraction over the 32 queries).
-        // The next tile's DMA goes out right after this tile's last LDS read:
-        // the compiler cannot tell that the DMA (into the other stage) and
-        // these reads do not overlap and would make any later read wait for
-        // it; here it overlaps the remaining products instead.
         static_for<0, 2 * DT>([&](auto step) {
             constexpr int i = decltype(step)::value;
             constexpr int c2 = i / DT, dt = i % DT;
@@ -539,40 +535,50 @@ flash_bwd_dkdv(const T* __restrict__ Q, const T* __restrict__ K, const T* __rest
             dva[dt] = M::run(ring[2 * (i % RB) + 0], bp[c2], dva[dt]);
             dka[dt] = M::run(ring[2 * (i % RB) + 1], bs[c2], dka[dt]);
             if constexpr (i + RB < 2 * DT) read2(Int<i + RB>{});
-            if constexpr (i + RB == 2 * DT - 1 || (RB >= 2 * DT && i == 0)) {
-                __builtin_amdgcn_sched_barrier(0);
-                after_reads();
-            }
         });
         __builtin_amdgcn_sched_barrier(0);
     };
 
-    // Stream (query head, query tile) pairs: heads g grp .. g grp + grp - 1.
-    const int qtiles = (n + BQ - 1) / BQ;
-    const int steps = grp * qtiles;
-    auto head_of = [&](int t) { return g * grp + t / qtiles; };
-    auto row_of = [&](int t) { return (t % qtiles) * BQ; };
-    // After tile t's last LDS read (see compute): the LSE/D store and the
-    // Q/dO DMA of tile t + 1 (its LSE/D loaded one tile earlier), then the
-    // LSE/D load of tile t + 2.  No global load is in flight while a tile
-    // computes, so waits for spill reloads there wait for nothing else.
-    issue_tile(head_of(0), row_of(0), Int<0>{}, load_lv(head_of(0), row_of(0)));
-    float lv_next = steps > 1 ? load_lv(head_of(1), row_of(1)) : 0.f;
+    // Stream (query head, query tile) pairs: heads g grp .. g grp + grp - 1,
+    // each over its query tiles.  Cursors (head, first row) of tiles t + 1 and
+    // t + 2 advance by one tile per step (no divisions in the loop).
+    const int steps = grp * ((n + BQ - 1) / BQ);
+    auto advance = [&](int& h, int& r) {
+        r += BQ;
+        if (r >= n) { r = 0; ++h; }
+    };
+    int h1 = g * grp, r1 = 0;
+    issue_tile(h1, r1, Int<0>{}, load_lv(h1, r1));
+    advance(h1, r1);
+    int h2 = h1, r2 = r1;
+    float lv_next = steps > 1 ? load_lv(h2, r2) : 0.f;
+    advance(h2, r2);
+    int r0 = 0;
+    // At the top of tile t (after the barrier, so every wave is done with
+    // the other stage): the LSE/D store and Q/dO DMA of tile t + 1 into the
+    // other stage (its LSE/D loaded one tile earlier), then the LSE/D load
+    // of tile t + 2; all land while tile t computes.
     auto next = [&](int t, auto stage) {
         if (t + 1 < steps) {
-            issue_tile(head_of(t + 1), row_of(t + 1), stage, lv_next);
-            if (t + 2 < steps) lv_next = load_lv(head_of(t + 2), row_of(t + 2));
+            issue_tile(h1, r1, stage, lv_next);
+            if (t + 2 < steps) lv_next = load_lv(h2, r2);
+            h1 = h2; r1 = r2;
+            advance(h2, r2);
         }
     };
     for (int t = 0;;) {
         __builtin_amdgcn_s_waitcnt(0x0070);   // vmcnt(0) lgkmcnt(0): own loads and LDS stores done
         __syncthreads();
-        compute(Int<0>{}, row_of(t), [&]() { next(t, Int<1>{}); });
+        next(t, Int<1>{});
+        compute(Int<0>{}, r0);
         if (++t == steps) break;
+        r0 = r0 + BQ >= n ? 0 : r0 + BQ;
         __builtin_amdgcn_s_waitcnt(0x0070);
         __syncthreads();
-        compute(Int<1>{}, row_of(t), [&]() { next(t, Int<0>{}); });
+        next(t, Int<0>{});
+        compute(Int<1>{}, r0);
         if (++t == steps) break;
+        r0 = r0 + BQ >= n ? 0 : r0 + BQ;
     }
 
     if (key < n) {
