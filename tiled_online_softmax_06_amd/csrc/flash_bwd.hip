@@ -237,6 +237,11 @@ flash_bwd_dq(const T* __restrict__ Q, const T* __restrict__ K, const T* __restri
 #pragma unroll
         for (int kt = 0; kt < KT; ++kt) { s[kt] = f32x16(0.f); dp[kt] = f32x16(0.f); }
         static_for<0, RQ>([&](auto i) { read1(i); });
+        // Matrix programs run at raised issue priority and the vector work at
+        // the normal one: on a SIMD shared with another workgroup's wave, a
+        // product whose operands are ready goes ahead of that wave's vector
+        // instructions.
+        __builtin_amdgcn_s_setprio(1);
         static_for<0, N1>([&](auto step) {
             constexpr int i = decltype(step)::value;
             constexpr int kt = i / KC, kc = i % KC;
@@ -246,6 +251,7 @@ flash_bwd_dq(const T* __restrict__ Q, const T* __restrict__ K, const T* __restri
             if constexpr (i + RQ < N1) read1(Int<i + RQ>{});
         });
         __builtin_amdgcn_sched_barrier(0);
+        __builtin_amdgcn_s_setprio(0);
         constexpr int N2 = PC * DT;
         auto read2 = [&](auto step) {
             constexpr int i = decltype(step)::value;
@@ -284,6 +290,7 @@ flash_bwd_dq(const T* __restrict__ Q, const T* __restrict__ K, const T* __restri
             bsv[pc] = M::pack(w);
         }
         // dQ^T += K^T dS^T.
+        __builtin_amdgcn_s_setprio(1);
         static_for<0, N2>([&](auto step) {
             constexpr int i = decltype(step)::value;
             constexpr int pc = i / DT, dt = i % DT;
@@ -292,6 +299,7 @@ flash_bwd_dq(const T* __restrict__ Q, const T* __restrict__ K, const T* __restri
             if constexpr (i + 2 * RQ < N2) read2(Int<i + 2 * RQ>{});
         });
         __builtin_amdgcn_sched_barrier(0);
+        __builtin_amdgcn_s_setprio(0);
     };
 
     const int ntiles = (n + BC - 1) / BC;
@@ -479,6 +487,11 @@ flash_bwd_dkdv(const T* __restrict__ Q, const T* __restrict__ K, const T* __rest
         // S = Q K^T and dP = dO V^T (queries x keys).
         f32x16 s = f32x16(0.f), dp = f32x16(0.f);
         static_for<0, RB>([&](auto i) { read1(i); });
+        // Matrix programs run at raised issue priority and the vector work at
+        // the normal one: on a SIMD shared with another workgroup's wave, a
+        // product whose operands are ready goes ahead of that wave's vector
+        // instructions.
+        __builtin_amdgcn_s_setprio(1);
         static_for<0, KC>([&](auto step) {
             constexpr int kc = decltype(step)::value;
             __builtin_amdgcn_sched_barrier(0);
@@ -487,6 +500,7 @@ flash_bwd_dkdv(const T* __restrict__ Q, const T* __restrict__ K, const T* __rest
             if constexpr (kc + RB < KC) read1(Int<kc + RB>{});
         });
         __builtin_amdgcn_sched_barrier(0);
+        __builtin_amdgcn_s_setprio(0);
         // dV/dK step i = c2 * DT + dt: operands tr(dO) and tr(Q), rows 16 c2.
         auto read2 = [&](auto step) {
             constexpr int i = decltype(step)::value;
@@ -528,6 +542,7 @@ flash_bwd_dkdv(const T* __restrict__ Q, const T* __restrict__ K, const T* __rest
         const u32x4 bp[2] = {M::pack(&p[0]), M::pack(&p[8])};
         const u32x4 bs[2] = {M::pack(&ds[0]), M::pack(&ds[8])};
         // dV^T += dO^T P and dK^T += Q^T dS (contraction over the 32 queries).
+        __builtin_amdgcn_s_setprio(1);
         static_for<0, 2 * DT>([&](auto step) {
             constexpr int i = decltype(step)::value;
             constexpr int c2 = i / DT, dt = i % DT;
@@ -537,6 +552,7 @@ flash_bwd_dkdv(const T* __restrict__ Q, const T* __restrict__ K, const T* __rest
             if constexpr (i + RB < 2 * DT) read2(Int<i + RB>{});
         });
         __builtin_amdgcn_sched_barrier(0);
+        __builtin_amdgcn_s_setprio(0);
     };
 
     // Stream (query head, query tile) pairs: heads g grp .. g grp + grp - 1,
