@@ -616,6 +616,308 @@ flash_bwd_dkdv(const T* __restrict__ Q, const T* __restrict__ K, const T* __rest
     }
 }
 
+// ---------------------------------------------------------------------------
+// dK, dV at d = 128 with two wave groups in alternating phases.  Workgroup:
+// 8 waves x 32 keys of one (b, K/V head), 256 keys; waves w and w + 4 share a
+// SIMD.  The 32-query tiles of Q and dO (with their LSE and D) stream through
+// a three-stage LDS ring.  Every wave runs MFMA phase j (S_j = Q_j K^T and
+// dP_j = dO_j V^T, then dV^T += dO_{j-1}^T P_{j-1} and dK^T += Q_{j-1}^T
+// dS_{j-1}), a workgroup barrier, vector phase j (P_j, dS_j), a barrier;
+// group 1 runs one phase behind group 0, so on every SIMD one wave feeds the
+// matrix core while the other computes exponentials.  Group 1 loads tile
+// j + 2 at the start of its vector phase j, into the stage of tile j - 1
+// (last read in its own MFMA phase j, one phase after group 0's), and waits
+// for the loads before the barrier that ends the phase; group 0 first reads
+// the tile two phases later.  No load is in flight during an MFMA phase.
+// ---------------------------------------------------------------------------
+template <typename T, int D>
+__global__ void __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2)))
+flash_bwd_dkdv_pp(const T* __restrict__ Q, const T* __restrict__ K, const T* __restrict__ V,
+                  const T* __restrict__ dO, const float* __restrict__ LSE, const float* __restrict__ Dr,
+                  T* __restrict__ dK, T* __restrict__ dV, int n, int ktiles, int total, float c, float scale,
+                  int nh, int grp)
+{
+    using M = Mfma<T>;
+    constexpr int NW = 8;
+    constexpr int BQ = 32;                   // queries per streamed tile
+    constexpr int BK = 32 * NW;              // keys per workgroup
+    constexpr int ROWB = D * 2;
+    constexpr int CPR = D / 8;
+    constexpr int RPU = 64 / CPR;
+    constexpr int QTILEB = BQ * ROWB;
+    constexpr int QUNITS = QTILEB / 1024;    // DMA units of a Q (or dO) tile
+    constexpr int VTILEB = BK * ROWB;
+    constexpr int VUNITS = VTILEB / 1024;
+    constexpr int DT = D / 32;
+    constexpr int KC = D / 16;
+    constexpr int RB = 2;                    // LDS operand read-ahead (steps)
+    static_assert(D == 128 && QUNITS == 8 && VUNITS % NW == 0 && 2 * BQ == 64, "tile shape");
+
+    // Stage s of the Q and dO tiles at s * QTILEB, of their LSE (log2 units)
+    // and D at s * 2 BQ; then the workgroup's V rows.
+    __shared__ __attribute__((aligned(1024))) char qs[3 * QTILEB];
+    __shared__ __attribute__((aligned(1024))) char os[3 * QTILEB];
+    __shared__ __attribute__((aligned(16))) float ls[3 * 2 * BQ];
+    __shared__ __attribute__((aligned(1024))) char vs[VTILEB];
+
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int group = wave >> 2;
+    const int gw = wave & 3;
+    const int col = lane & 31;
+    const int half = lane >> 5;
+
+    const int tile = xcd_tile(blockIdx.x, total);
+    const int bkv = tile / ktiles;           // b * Hkv + g
+    const int kt0 = (tile - bkv * ktiles) * BK;
+    const int nkv = nh / grp;
+    const int b = bkv / nkv, g = bkv - b * nkv;
+    const int64_t kvbase = (int64_t)bkv * n * D;
+    const int key = kt0 + wave * 32 + col;   // this lane's key (column of S)
+    const int keyc = min(key, n - 1);
+
+    // K^T as the B operand of S = Q K^T: lane (col, half) holds K[key][16 kc +
+    // 8 half + 0..7].
+    u32x4 kf[KC];
+    {
+        const T* kp = K + kvbase + (int64_t)keyc * D + 8 * half;
+#pragma unroll
+        for (int kc = 0; kc < KC; ++kc) kf[kc] = *(const u32x4*)(kp + 16 * kc);
+    }
+
+    const int lrow = lane / CPR;
+    const int lch = lane % CPR;
+    // V rows of the workgroup's keys (rows past the end re-read the last row).
+    {
+        const __amdgpu_buffer_rsrc_t vrs =
+            __builtin_amdgcn_make_buffer_rsrc((void*)(V + kvbase), (short)0, n * ROWB, 0x00020000);
+#pragma unroll
+        for (int i = 0; i < VUNITS / NW; ++i) {
+            const int u = wave * (VUNITS / NW) + i;
+            const int r = u * RPU + lrow;
+            dma16(vrs, vs + u * 1024, min(kt0 + r, n - 1) * ROWB + 16 * (lch ^ swz_k<D>(r)), 0);
+        }
+    }
+
+    // Loads of group 1.  load_lv: wave 4 reads a tile's LSE (lanes 0..31) and
+    // D (lanes 32..63) into a register; issue_tile: its LSE / D into LDS
+    // (first: a store after the DMAs would wait for them), then the Q and dO
+    // units gw and gw + 4 of the tile.  Per-lane offsets come from an opaque
+    // copy of the lane index, so that they are not kept across the loop.
+    auto load_lv = [&](int h, int i0) {
+        float lv = 0.f;
+        if (wave == 4) {
+            int ln;
+            asm volatile("v_mov_b32 %0, %1" : "=v"(ln) : "v"(lane));
+            const int64_t rowi = ((int64_t)b * nh + h) * n + min(i0 + (ln & (BQ - 1)), n - 1);
+            lv = (ln < BQ ? LSE : Dr)[rowi];
+        }
+        return lv;
+    };
+    auto issue_tile = [&](int h, int i0, int st, float lv) {
+        int ln;
+        asm volatile("v_mov_b32 %0, %1" : "=v"(ln) : "v"(lane));
+        const int lr = ln / CPR, lc = ln % CPR;
+        if (wave == 4) ls[st * 2 * BQ + ln] = ln < BQ ? lv * 1.4426950408889634f : lv;
+        const int64_t qbase = ((int64_t)b * nh + h) * n * D;
+        const __amdgpu_buffer_rsrc_t qrs =
+            __builtin_amdgcn_make_buffer_rsrc((void*)(Q + qbase), (short)0, n * ROWB, 0x00020000);
+        const __amdgpu_buffer_rsrc_t ors =
+            __builtin_amdgcn_make_buffer_rsrc((void*)(dO + qbase), (short)0, n * ROWB, 0x00020000);
+#pragma unroll
+        for (int k = 0; k < 2; ++k) {
+            const int u = gw + 4 * k;
+            const int r = u * RPU + lr;
+            const int gofs = min(i0 + r, n - 1) * ROWB + 16 * (lc ^ swz_rt<D>(r));
+            dma16(qrs, qs + st * QTILEB + u * 1024, gofs, 0);
+            dma16(ors, os + st * QTILEB + u * 1024, gofs, 0);
+        }
+    };
+
+    // LDS read offsets (as in flash_bwd_dkdv); the stage offsets are
+    // multiples of 8 KiB, which the XOR forms leave untouched.
+    const int qoff = col * ROWB + 16 * (half ^ swz_rt<D>(col));
+    const int voff = (wave * 32 + col) * ROWB + 16 * (half ^ swz_k<D>(col));
+    const int qtr = tr_offset0<D>(lane);
+
+    f32x16 dka[DT], dva[DT];   // dK^T, dV^T (d x keys)
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt) { dka[dt] = f32x16(0.f); dva[dt] = f32x16(0.f); }
+    f32x16 s = f32x16(0.f), dp = f32x16(0.f);   // S and dP of the current tile
+    u32x4 bp[2], bs[2];                         // P and dS of the previous tile (B operands)
+    u32x4 ring[3 * RB];
+
+    // MFMA phase as a fixed program: S/dP steps kc (Q row x K, dO row x V),
+    // then dV/dK steps (c2, dt) (transposed dO and Q of the previous tile).
+    auto mphase = [&](int stc, int stp, auto has_sdp, auto has_dvdk) {
+        constexpr int N1 = decltype(has_sdp)::value ? KC : 0;
+        constexpr int N2 = decltype(has_dvdk)::value ? 2 * DT : 0;
+        constexpr int NS = N1 + N2;
+        int qo = qoff + stc * QTILEB, vo = voff, to = qtr + stp * QTILEB;
+        asm volatile("" : "+v"(qo), "+v"(vo), "+v"(to));
+        auto read = [&](auto step) {
+            constexpr int i = decltype(step)::value;
+            if constexpr (i < N1) {
+                ring[3 * (i % RB) + 0] = *(const u32x4*)(qs + (qo ^ (32 * i)));
+                ring[3 * (i % RB) + 1] = *(const u32x4*)(os + (qo ^ (32 * i)));
+                ring[3 * (i % RB) + 2] = *(const u32x4*)(vs + (vo ^ (32 * i)));
+            } else {
+                constexpr int k = i - N1, c2 = k / DT, dt = k % DT;
+                ring[3 * (i % RB) + 0] = read_tr<ROWB>(os, 16 * c2, to, dt);
+                ring[3 * (i % RB) + 1] = read_tr<ROWB>(qs, 16 * c2, to, dt);
+            }
+        };
+        auto mma = [&](auto step) {
+            constexpr int i = decltype(step)::value;
+            if constexpr (i < N1) {
+                s = M::run(ring[3 * (i % RB) + 0], kf[i], i == 0 ? f32x16(0.f) : s);
+                dp = M::run(ring[3 * (i % RB) + 1], ring[3 * (i % RB) + 2], i == 0 ? f32x16(0.f) : dp);
+            } else {
+                constexpr int k = i - N1, c2 = k / DT, dt = k % DT;
+                dva[dt] = M::run(ring[3 * (i % RB) + 0], bp[c2], dva[dt]);
+                dka[dt] = M::run(ring[3 * (i % RB) + 1], bs[c2], dka[dt]);
+            }
+        };
+        __builtin_amdgcn_s_setprio(1);
+        static_for<0, (RB < NS ? RB : NS)>([&](auto i) { read(i); });
+        static_for<0, NS>([&](auto step) {
+            constexpr int i = decltype(step)::value;
+            __builtin_amdgcn_sched_barrier(0);
+            mma(step);
+            if constexpr (i + RB < NS) read(Int<i + RB>{});
+        });
+        __builtin_amdgcn_sched_barrier(0);
+        __builtin_amdgcn_s_setprio(0);
+        __builtin_amdgcn_sched_barrier(0);
+    };
+
+    // Vector phase: P = exp2(S c - LSE log2 e), dS = P (dP - D), packed as the
+    // next MFMA phase's B operands.  Register r holds query row 8 (r / 4) +
+    // 4 half + r % 4; rows past the end get P = dS = 0 (set, not multiplied:
+    // their LSE and D slots need not be finite), in a branch taken by a
+    // ragged last query tile only.
+    auto vphase = [&](int st, int i0) {
+        const float* lb = ls + st * 2 * BQ;
+        float p[16], ds[16];
+#pragma unroll
+        for (int q4 = 0; q4 < 4; ++q4) {
+            const float4 l4 = *(const float4*)(lb + 8 * q4 + 4 * half);
+            const float4 d4 = *(const float4*)(lb + BQ + 8 * q4 + 4 * half);
+            const float lv[4] = {l4.x, l4.y, l4.z, l4.w};
+            const float dv[4] = {d4.x, d4.y, d4.z, d4.w};
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int r = 4 * q4 + e;
+                const float pr = __builtin_amdgcn_exp2f(fmaf(s[r], c, -lv[e]));
+                p[r] = pr;
+                ds[r] = pr * (dp[r] - dv[e]);
+            }
+        }
+        if (i0 + BQ > n) {
+            asm volatile("");
+            const int lim = n - i0 - 4 * half;
+#pragma unroll
+            for (int r = 0; r < 16; ++r)
+                if (8 * (r >> 2) + (r & 3) >= lim) {
+                    p[r] = 0.f;
+                    ds[r] = 0.f;
+                }
+        }
+        bp[0] = M::pack(&p[0]);
+        bp[1] = M::pack(&p[8]);
+        bs[0] = M::pack(&ds[0]);
+        bs[1] = M::pack(&ds[8]);
+        // keep the vector work inside its phase
+        asm volatile("" : "+v"(bp[0]), "+v"(bp[1]), "+v"(bs[0]), "+v"(bs[1]));
+    };
+
+    auto phase_barrier = [&]() {
+        __builtin_amdgcn_sched_barrier(0);
+        asm volatile("" ::: "memory");
+        __builtin_amdgcn_s_barrier();
+        asm volatile("" ::: "memory");
+        __builtin_amdgcn_sched_barrier(0);
+    };
+
+    // Stream (query head, query tile) pairs: heads g grp .. g grp + grp - 1,
+    // each over its query tiles; cursors advance one tile per step.
+    const int steps = grp * ((n + BQ - 1) / BQ);
+    auto advance = [&](int& h, int& r) {
+        r += BQ;
+        if (r >= n) { r = 0; ++h; }
+    };
+    int hn = g * grp, rn = 0;                // next tile to load (group 1)
+    float lv_next = 0.f;                     // its LSE / D (wave 4)
+    if (group == 1) {
+        issue_tile(hn, rn, 0, load_lv(hn, rn));
+        advance(hn, rn);
+        if (steps > 1) {
+            issue_tile(hn, rn, 1, load_lv(hn, rn));
+            advance(hn, rn);
+        }
+        if (steps > 2) lv_next = load_lv(hn, rn);
+    }
+    __builtin_amdgcn_s_waitcnt(0x0070);   // vmcnt(0) lgkmcnt(0): K, V, tiles 0 and 1 landed
+    phase_barrier();
+    if (group == 1) phase_barrier();     // group 1 runs one phase behind
+
+    int rv = 0;                              // first row of the vector phase's tile
+    // Vector phase j: group 1 first issues the loads of tile j + 2 (into
+    // stage st2) and of the LSE / D of tile j + 3, then both groups take P
+    // and dS; each wave waits for all its loads before the phase-ending
+    // barrier, so no load is in flight during the next MFMA phase.
+    auto vtail = [&](int j, int stc, int st2, auto has_sdp) {
+        if (group == 1 && j + 2 < steps) {
+            issue_tile(hn, rn, st2, lv_next);
+            advance(hn, rn);
+            if (j + 3 < steps) lv_next = load_lv(hn, rn);
+        }
+        if constexpr (decltype(has_sdp)::value) {
+            vphase(stc, rv);
+            rv = rv + BQ >= n ? 0 : rv + BQ;
+        }
+        __builtin_amdgcn_s_waitcnt(0x0070);   // vmcnt(0) lgkmcnt(0)
+        phase_barrier();
+    };
+
+    using F = Int<0>;
+    using Tr = Int<1>;
+    // tile j lives in stage j mod 3; tile j + 2 goes into the stage of j - 1
+    mphase(0, 0, Tr{}, F{});
+    phase_barrier();
+    vtail(0, 0, 2, Tr{});
+    int stc = 1, stp = 0;
+    for (int j = 1; j < steps; ++j) {
+        mphase(stc, stp, Tr{}, Tr{});
+        phase_barrier();
+        vtail(j, stc, stp, Tr{});
+        stp = stc;
+        stc = stc == 2 ? 0 : stc + 1;
+    }
+    mphase(0, stp, F{}, Tr{});
+    phase_barrier();
+    vtail(steps, 0, 0, F{});
+    if (group == 0) phase_barrier();
+
+    if (key < n) {
+        T* krow = dK + kvbase + (int64_t)key * D;
+        T* vrow_out = dV + kvbase + (int64_t)key * D;
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+            for (int gq = 0; gq < 4; ++gq) {
+                float k4[4], v4[4];
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    k4[e] = dka[dt][4 * gq + e] * scale;
+                    v4[e] = dva[dt][4 * gq + e];
+                }
+                *(u32x2*)(krow + 32 * dt + 8 * gq + 4 * half) = M::pack4(k4);
+                *(u32x2*)(vrow_out + 32 * dt + 8 * gq + 4 * half) = M::pack4(v4);
+            }
+    }
+}
+
 template <typename T, int D>
 hipError_t launch_bwd_t(const BwdArgs& a, hipStream_t stream) {
     const int n = (int)a.n;
@@ -655,13 +957,18 @@ hipError_t launch_bwd_t(const BwdArgs& a, hipStream_t stream) {
         hipError_t e = hipLaunchKernel((const void*)&flash_bwd_dq<T, D>, dim3(total), dim3(256), args, 0, stream);
         if (e != hipSuccess) return e;
     }
-    // 3. dK, dV
+    // 3. dK, dV: at d = 128 the two-group kernel (256 keys per workgroup),
+    // at d = 64 the four-wave one (128 keys per workgroup)
     {
-        const int ktiles = (int)((a.n + 127) / 128);
+        const int bk = D == 128 ? 256 : 128;
+        const int ktiles = (int)((a.n + bk - 1) / bk);
         const int total = (int)((a.bh / grp) * ktiles);
         void* args[] = {&q, &k, &v, &dout, &lse, &dr, &dk, &dv, (void*)&n, (void*)&ktiles, (void*)&total,
                         (void*)&c, (void*)&scale, (void*)&nh, (void*)&grp};
-        return hipLaunchKernel((const void*)&flash_bwd_dkdv<T, D>, dim3(total), dim3(256), args, 0, stream);
+        if constexpr (D == 128)
+            return hipLaunchKernel((const void*)&flash_bwd_dkdv_pp<T, D>, dim3(total), dim3(512), args, 0, stream);
+        else
+            return hipLaunchKernel((const void*)&flash_bwd_dkdv<T, D>, dim3(total), dim3(256), args, 0, stream);
     }
 }
 
