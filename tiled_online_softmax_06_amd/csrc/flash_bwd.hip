@@ -899,23 +899,41 @@ flash_bwd_dkdv_pp(const T* __restrict__ Q, const T* __restrict__ K, const T* __r
     vtail(steps, 0, 0, F{});
     if (group == 0) phase_barrier();
 
-    if (key < n) {
-        T* krow = dK + kvbase + (int64_t)key * D;
-        T* vrow_out = dV + kvbase + (int64_t)key * D;
+    // Lane (col, half) holds elements 8 gq + 4 half + 0..3 of each 32-wide
+    // chunk dt of its key's row.  A swap between lanes col and col + 32 gives
+    // half 0 all 8 elements of gq = 2 m and half 1 those of gq = 2 m + 1, so
+    // each lane stores 16 contiguous bytes and each instruction fills whole
+    // 32-byte segments of the rows.
+    // The row address comes from an opaque copy of the lane index, so that
+    // nothing of it is kept in registers across the tile loop.
+    int ln;
+    asm volatile("v_mov_b32 %0, %1" : "=v"(ln) : "v"(lane));
+    const int skey = kt0 + wave * 32 + (ln & 31);
+    const int64_t srow = kvbase + (int64_t)min(skey, n - 1) * D + 8 * (ln >> 5);
+    auto store_row = [&](T* row, const f32x16* acc, float f) __attribute__((always_inline)) {
 #pragma unroll
         for (int dt = 0; dt < DT; ++dt)
 #pragma unroll
-            for (int gq = 0; gq < 4; ++gq) {
-                float k4[4], v4[4];
+            for (int m = 0; m < 2; ++m) {
+                float lo[4], hi[4];
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
-                    k4[e] = dka[dt][4 * gq + e] * scale;
-                    v4[e] = dva[dt][4 * gq + e];
+                    lo[e] = acc[dt][8 * m + e] * f;
+                    hi[e] = acc[dt][8 * m + 4 + e] * f;
                 }
-                *(u32x2*)(krow + 32 * dt + 8 * gq + 4 * half) = M::pack4(k4);
-                *(u32x2*)(vrow_out + 32 * dt + 8 * gq + 4 * half) = M::pack4(v4);
+                const u32x2 a = M::pack4(lo), bb = M::pack4(hi);
+                const auto s0 = __builtin_amdgcn_permlane32_swap(a.x, bb.x, false, false);
+                const auto s1 = __builtin_amdgcn_permlane32_swap(a.y, bb.y, false, false);
+                u32x4 out;
+                out.x = s0[0];
+                out.y = s1[0];
+                out.z = s0[1];
+                out.w = s1[1];
+                if (skey < n) *(u32x4*)(row + 32 * dt + 16 * m) = out;
             }
-    }
+    };
+    store_row(dK + srow, dka, scale);
+    store_row(dV + srow, dva, 1.f);
 }
 
 template <typename T, int D>
