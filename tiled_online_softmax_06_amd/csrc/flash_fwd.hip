@@ -117,16 +117,21 @@ flash_fwd_16(const T* __restrict__ Q, const T* __restrict__ K, const T* __restri
     const int qrow = qt * BR + wave * 32 + col;
 
     // Q^T as the B operand: lane (col, half) holds Q[qrow][16*kc + 8*half + 0..7]
-    // (rows past the end are clamped: computed, never stored).
+    // (rows past the end are clamped: computed, never stored).  A negative
+    // scale flips the sign bits of Q, after the first K/V tile's DMA has been
+    // issued (done here, the flip would make that DMA wait for Q to arrive).
     u32x4 qf[KC];
     {
         const T* qp = Q + base + (int64_t)min(qrow, n - 1) * D + 8 * half;
 #pragma unroll
-        for (int kc = 0; kc < KC; ++kc) {
-            qf[kc] = *(const u32x4*)(qp + 16 * kc);
-            if (negate) qf[kc] ^= u32x4(0x80008000u);
-        }
+        for (int kc = 0; kc < KC; ++kc) qf[kc] = *(const u32x4*)(qp + 16 * kc);
     }
+    auto negate_q = [&]() {
+        if (negate) {
+#pragma unroll
+            for (int kc = 0; kc < KC; ++kc) qf[kc] ^= u32x4(0x80008000u);
+        }
+    };
 
     // Per-head buffer resources: any offset past the head reads zero instead
     // of faulting (the tail below also clamps, so this is a safety net).
@@ -314,6 +319,7 @@ flash_fwd_16(const T* __restrict__ Q, const T* __restrict__ K, const T* __restri
         constexpr int g = decltype(G)::value;
         auto has = [&](int i) { return KS * i + g < ntiles; };
         if (has(0)) issue_loads(g * BC, G, Int<0>{});
+        negate_q();
         for (int i = 0;;) {
             __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0): this wave's DMA landed
             __syncthreads();                      // ... every wave's; stage 1 is free

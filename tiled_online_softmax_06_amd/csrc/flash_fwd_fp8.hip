@@ -131,21 +131,25 @@ flash_fwd_fp8(const uint8_t* __restrict__ Q, const uint8_t* __restrict__ K, cons
 
     // Q^T as the B operand: lane (col, half) holds Q[qrow][64 kc + 32 half +
     // 0..31]; rows past the end are clamped (computed, never stored).  A
-    // negative scale flips the sign bits of Q (e4m3: bit 7).
+    // negative scale flips the sign bits of Q (e4m3: bit 7), after the first
+    // K/V tile's DMA has been issued (done here, the flip would make that DMA
+    // wait for Q to arrive).
     i32x8 qf[KC];
     {
         const uint8_t* qp = Q + base + (int64_t)min(qrow, n - 1) * D + 32 * half;
 #pragma unroll
         for (int kc = 0; kc < KC; ++kc) {
-            u32x4 lo = *(const u32x4*)(qp + 64 * kc);
-            u32x4 hi = *(const u32x4*)(qp + 64 * kc + 16);
-            if (negate) {
-                lo ^= u32x4(0x80808080u);
-                hi ^= u32x4(0x80808080u);
-            }
+            const u32x4 lo = *(const u32x4*)(qp + 64 * kc);
+            const u32x4 hi = *(const u32x4*)(qp + 64 * kc + 16);
             qf[kc] = i32x8{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
         }
     }
+    auto negate_q = [&]() {
+        if (negate) {
+#pragma unroll
+            for (int kc = 0; kc < KC; ++kc) qf[kc] ^= i32x8(0x80808080);
+        }
+    };
 
     const __amdgpu_buffer_rsrc_t krs =
         __builtin_amdgcn_make_buffer_rsrc((void*)(K + kvbase), (short)0, n * ROWB, 0x00020000);
@@ -312,6 +316,7 @@ flash_fwd_fp8(const uint8_t* __restrict__ Q, const uint8_t* __restrict__ K, cons
 
     const int ntiles = (n + BC - 1) / BC;
     issue_loads(0, Int<0>{});
+    negate_q();
     for (int t = 0;;) {
         __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0): this wave's DMA landed
         __syncthreads();                      // ... every wave's; stage 1 is free
