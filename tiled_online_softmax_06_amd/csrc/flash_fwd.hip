@@ -84,7 +84,7 @@ flash_fwd_16(const T* __restrict__ Q, const T* __restrict__ K, const T* __restri
     static_assert(UNITS % NW == 0 && BC % 32 == 0, "tile shape");
 
     static_assert(KS == 1 || KS == 2, "key groups");
-    constexpr int TILEB2 = KS > 1 ? TILEB : 16;
+    constexpr int TILEB3 = KS > 1 ? TILEB : 16;
 
     // Separate objects per stage, operand and key group, so the compiler can
     // see that the DMA into one stage never aliases the reads of another.
@@ -92,10 +92,10 @@ flash_fwd_16(const T* __restrict__ Q, const T* __restrict__ K, const T* __restri
     __shared__ __attribute__((aligned(1024))) char vs0[TILEB];
     __shared__ __attribute__((aligned(1024))) char ks1[TILEB];
     __shared__ __attribute__((aligned(1024))) char vs1[TILEB];
-    __shared__ __attribute__((aligned(1024))) char ks2[TILEB2];
-    __shared__ __attribute__((aligned(1024))) char vs2[TILEB2];
-    __shared__ __attribute__((aligned(1024))) char ks3[TILEB2];
-    __shared__ __attribute__((aligned(1024))) char vs3[TILEB2];
+    __shared__ __attribute__((aligned(1024))) char ks2[TILEB];
+    __shared__ __attribute__((aligned(1024))) char vs2[TILEB];
+    __shared__ __attribute__((aligned(1024))) char ks3[TILEB3];
+    __shared__ __attribute__((aligned(1024))) char vs3[TILEB3];
 
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane((threadIdx.x >> 6) % NW);   // row block
@@ -151,34 +151,33 @@ flash_fwd_16(const T* __restrict__ Q, const T* __restrict__ K, const T* __restri
         vvo[i] = r * ROWB + 16 * (lch ^ swz_v<D>(r));
     }
 
-    // LDS stages of key group G (compile time): stage 0 / 1 of K and V.
+    // LDS stages of key group G (compile time): KS = 1, stages 0 / 1 / 2 in
+    // ks0..2 (vs0..2); KS = 2, group 0 in ks0 / ks1 and group 1 in ks2 / ks3.
     auto kst = [&](auto G, auto stage) -> char* {
         constexpr int g = decltype(G)::value, st = decltype(stage)::value;
-        return g ? (st ? ks3 : ks2) : (st ? ks1 : ks0);
+        return g ? (st ? ks3 : ks2) : (st == 0 ? ks0 : st == 1 ? ks1 : ks2);
     };
     auto vst = [&](auto G, auto stage) -> char* {
         constexpr int g = decltype(G)::value, st = decltype(stage)::value;
-        return g ? (st ? vs3 : vs2) : (st ? vs1 : vs0);
+        return g ? (st ? vs3 : vs2) : (st == 0 ? vs0 : st == 1 ? vs1 : vs2);
     };
+    // First key held by the LDS tile of the tile at key j0: j0 itself for a
+    // full tile; for the ragged last tile (j0 > 0) the window is moved back
+    // to end at the last key, nk - BC, and its rows below j0 are masked (they
+    // belong to the previous tile); a range shorter than one tile starts at
+    // 0 and its rows past the end read zeros (the per-lane offset is bounds
+    // checked).  Tiles past the end load the last window again (never read).
+    // So every DMA has one form: per-lane offsets fixed for the kernel plus a
+    // wave-uniform tile offset, with nothing to branch on.
+    auto tile_base = [&](int j0) { return min(j0, max(nk - BC, 0)); };
     auto issue_loads = [&](int j0, auto G, auto stage) {
         char* kdst = kst(G, stage) + wave * UPW * 1024;
         char* vdst = vst(G, stage) + wave * UPW * 1024;
-        if (j0 + BC <= nk) {
+        const int so = tile_base(j0) * ROWB;
 #pragma unroll
-            for (int i = 0; i < UPW; ++i) {
-                dma16(krs, kdst + i * 1024, kvo[i], j0 * ROWB);
-                dma16(vrs, vdst + i * 1024, vvo[i], j0 * ROWB);
-            }
-        } else {
-            // Ragged last tile: rows past the end re-read the last row (finite
-            // values; their scores are masked and their weights are zero).
-#pragma unroll
-            for (int i = 0; i < UPW; ++i) {
-                const int r = (wave * UPW + i) * RPU + lrow;
-                const int g = min(j0 + r, nk - 1) * ROWB;
-                dma16(krs, kdst + i * 1024, g + 16 * (lch ^ swz_k<D>(r)), 0);
-                dma16(vrs, vdst + i * 1024, g + 16 * (lch ^ swz_v<D>(r)), 0);
-            }
+        for (int i = 0; i < UPW; ++i) {
+            dma16(krs, kdst + i * 1024, kvo[i], so);
+            dma16(vrs, vdst + i * 1024, vvo[i], so);
         }
     };
 
@@ -246,13 +245,18 @@ flash_fwd_16(const T* __restrict__ Q, const T* __restrict__ K, const T* __restri
         __builtin_amdgcn_sched_barrier(0);
         static_for<0, (R16 < N2 ? R16 : N2)>([&](auto i) { read2(i); });
 
-        const bool ragged = j0 + BC > nk;
-        if (ragged) {
+        // ragged last tile: only LDS rows [lo, hi) hold keys of this tile
+        // (register r of lane half h holds row 32 kt + 8 (r >> 2) + (r & 3) + 4 h)
+        if (j0 + BC > nk) {
+            const int kb = tile_base(j0);
+            const int lo = j0 - kb - 4 * half, hi = nk - kb - 4 * half;
 #pragma unroll
             for (int kt = 0; kt < KT; ++kt)
 #pragma unroll
-                for (int r = 0; r < 16; ++r)
-                    if (j0 + 32 * kt + acc_row(r, half) >= nk) s[kt][r] = -INFINITY;
+                for (int r = 0; r < 16; ++r) {
+                    const int row = 32 * kt + 8 * (r >> 2) + (r & 3);
+                    if (row < lo || row >= hi) s[kt][r] = -INFINITY;
+                }
         }
 
         // Weights against the current reference max first; the tile max, the
@@ -333,8 +337,43 @@ flash_fwd_16(const T* __restrict__ Q, const T* __restrict__ K, const T* __restri
             if (++i == nsteps) break;
         }
     };
+    // KS = 1 (several workgroups per CU): three stages, the DMA of tile t + 2
+    // issued at the top of step t into the stage of tile t - 1, which every
+    // wave finished reading in step t - 1; each wave waits only for tile t's
+    // DMA (tile t + 1's may still be in flight) before the barrier, which
+    // carries no fence (a fence would wait for every load).  Tiles past the
+    // end are loaded too (never read), so every step has the same loads in
+    // flight; with one DMA form and one loop exit the compiler's tracking of
+    // them stays exact and adds no waits of its own.
+    auto sweep3 = [&]() {
+        issue_loads(0, Int<0>{}, Int<0>{});
+        issue_loads(BC, Int<0>{}, Int<1>{});
+        negate_q();
+        static_assert(2 * UPW == 4, "wait count below");
+        auto stepk = [&](int t, auto stage) __attribute__((always_inline)) {
+            constexpr int S = decltype(stage)::value;
+            __builtin_amdgcn_s_waitcnt(0x0074);   // vmcnt(4) lgkmcnt(0): tile t landed
+            __builtin_amdgcn_sched_barrier(0);
+            asm volatile("" ::: "memory");
+            __builtin_amdgcn_s_barrier();
+            asm volatile("" ::: "memory");
+            __builtin_amdgcn_sched_barrier(0);
+            issue_loads((t + 2) * BC, Int<0>{}, Int<(S + 2) % 3>{});
+            compute(Int<0>{}, Int<S>{}, t * BC, t == 0);
+        };
+        stepk(0, Int<0>{});
+        int t = 1;
+        for (; t + 3 <= ntiles; t += 3) {
+            stepk(t, Int<1>{});
+            stepk(t + 1, Int<2>{});
+            stepk(t + 2, Int<0>{});
+        }
+        if (t < ntiles) stepk(t++, Int<1>{});
+        if (t < ntiles) stepk(t++, Int<2>{});
+        __builtin_amdgcn_s_waitcnt(0x0070);       // no DMA into LDS left in flight
+    };
     if constexpr (KS == 1) {
-        sweep(Int<0>{});
+        sweep3();
     } else {
         if (kgrp == 0) sweep(Int<0>{});
         else sweep(Int<1>{});
