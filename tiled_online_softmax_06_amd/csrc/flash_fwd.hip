@@ -537,24 +537,21 @@ flash_fwd_pp(const T* __restrict__ Q, const T* __restrict__ K, const T* __restri
     // swizzles (chosen by the global chunk each lane fetches).
     const int lrow = lane / CPR;
     const int lch = lane % CPR;
+    // One DMA form for every tile: fixed per-lane offsets plus a wave-uniform
+    // tile offset.  The ragged last tile's LDS window ends at the last key
+    // (its rows below the tile's first key are masked in the softmax); a
+    // range shorter than one tile reads zeros past its end (the per-lane
+    // offset is bounds checked).
+    auto tile_base = [&](int j0) { return min(j0, max(nk - BC, 0)); };
     auto issue = [&](__amdgpu_buffer_rsrc_t rs, char* stage, int j0, auto isk) {
         constexpr bool IK = decltype(isk)::value;
         char* dst = stage + gw * UPW * 1024;
-        if (j0 + BC <= nk) {
+        const int so = tile_base(j0) * ROWB;
 #pragma unroll
-            for (int i = 0; i < UPW; ++i) {
-                const int r = (gw * UPW + i) * RPU + lrow;
-                const int sw = IK ? swz_k<D>(r) : swz_v<D>(r);
-                dma16(rs, dst + i * 1024, r * ROWB + 16 * (lch ^ sw), j0 * ROWB);
-            }
-        } else {
-            // ragged last tile: rows past the end re-read the last row
-#pragma unroll
-            for (int i = 0; i < UPW; ++i) {
-                const int r = (gw * UPW + i) * RPU + lrow;
-                const int sw = IK ? swz_k<D>(r) : swz_v<D>(r);
-                dma16(rs, dst + i * 1024, min(j0 + r, nk - 1) * ROWB + 16 * (lch ^ sw), 0);
-            }
+        for (int i = 0; i < UPW; ++i) {
+            const int r = (gw * UPW + i) * RPU + lrow;
+            const int sw = IK ? swz_k<D>(r) : swz_v<D>(r);
+            dma16(rs, dst + i * 1024, r * ROWB + 16 * (lch ^ sw), so);
         }
     };
 
@@ -667,13 +664,17 @@ flash_fwd_pp(const T* __restrict__ Q, const T* __restrict__ K, const T* __restri
     // (about 20 vector instructions per tile) is computed only on the rare
     // tiles that need it.
     auto softmax = [&](int j0, auto first) {
+        // ragged last tile: only LDS rows [lo, hi) hold keys of this tile
         if (j0 + BC > nk) {
+            const int kb = tile_base(j0);
 #pragma unroll
             for (int kt = 0; kt < KT; ++kt) {
-                const int lim = nk - j0 - 32 * kt - 4 * half;
+                const int lo = j0 - kb - 32 * kt - 4 * half, hi = nk - kb - 32 * kt - 4 * half;
 #pragma unroll
-                for (int r = 0; r < 16; ++r)
-                    if (8 * (r >> 2) + (r & 3) >= lim) s[kt][r] = -INFINITY;
+                for (int r = 0; r < 16; ++r) {
+                    const int row = 8 * (r >> 2) + (r & 3);
+                    if (row < lo || row >= hi) s[kt][r] = -INFINITY;
+                }
             }
         }
         // Raise the reference max to this tile's max (both lanes of a query
