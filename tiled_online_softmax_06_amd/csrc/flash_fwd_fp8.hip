@@ -161,8 +161,7 @@ flash_fwd_fp8(const uint8_t* __restrict__ Q, const uint8_t* __restrict__ K, cons
     // Per-lane DMA offsets within a tile: LDS row r of unit i is key r of
     // the K tile and key rv of the V tile (r with bits 2 and 3 swapped, the
     // order in which P leaves the score accumulators; see the P.V product),
-    // at its swizzled chunk.  A full tile adds its byte offset as the scalar
-    // offset; the ragged last tile clamps its keys to the last row.
+    // at its swizzled chunk; the tile's byte offset is the scalar offset.
     int kdo[UPW], vdo[UPW];
 #pragma unroll
     for (int i = 0; i < UPW; ++i) {
@@ -171,25 +170,22 @@ flash_fwd_fp8(const uint8_t* __restrict__ Q, const uint8_t* __restrict__ K, cons
         kdo[i] = r * ROWB + 16 * (lch ^ swz8_k<D>(r));
         vdo[i] = rv * ROWB + 16 * (lch ^ swz8_v<D>(r));
     }
+    // One DMA form for every tile: the fixed per-lane offsets plus a
+    // wave-uniform tile offset.  The ragged last tile (j0 > 0) moves its
+    // window back to end at the last key, n - BC (its rows below j0 are
+    // masked, they belong to the previous tile); a sequence shorter than a
+    // tile starts at 0 and its rows past the end read zeros (the per-lane
+    // offset is bounds checked).
+    auto tile_base = [&](int j0) { return min(j0, max(n - BC, 0)); };
     auto issue_loads = [&](int j0, auto stage) {
         constexpr int st = decltype(stage)::value;
         char* kdst = (st ? ks1 : ks0) + wave * UPW * 1024;
         char* vdst = (st ? vs1 : vs0) + wave * UPW * 1024;
-        if (j0 + BC <= n) {
-            const int so = __builtin_amdgcn_readfirstlane(j0 * ROWB);
+        const int so = __builtin_amdgcn_readfirstlane(tile_base(j0) * ROWB);
 #pragma unroll
-            for (int i = 0; i < UPW; ++i) {
-                dma16(krs, kdst + i * 1024, kdo[i], so);
-                dma16(vrs, vdst + i * 1024, vdo[i], so);
-            }
-        } else {
-#pragma unroll
-            for (int i = 0; i < UPW; ++i) {
-                const int r = (wave * UPW + i) * RPU + lrow;
-                const int rv = (r & ~12) | ((r & 4) << 1) | ((r & 8) >> 1);
-                dma16(krs, kdst + i * 1024, min(j0 + r, n - 1) * ROWB + 16 * (lch ^ swz8_k<D>(r)), 0);
-                dma16(vrs, vdst + i * 1024, min(j0 + rv, n - 1) * ROWB + 16 * (lch ^ swz8_v<D>(r)), 0);
-            }
+        for (int i = 0; i < UPW; ++i) {
+            dma16(krs, kdst + i * 1024, kdo[i], so);
+            dma16(vrs, vdst + i * 1024, vdo[i], so);
         }
     };
 
@@ -241,12 +237,16 @@ flash_fwd_fp8(const uint8_t* __restrict__ Q, const uint8_t* __restrict__ K, cons
         // every tile executes).
         if (j0 + BC > n) {
             asm volatile("");
+            // only LDS rows [lo, hi) of the ragged tile hold its keys
+            const int kb0 = tile_base(j0);
 #pragma unroll
             for (int kt = 0; kt < KT; ++kt) {
-                const int lim = n - j0 - 32 * kt - 4 * half;
+                const int lo = j0 - kb0 - 32 * kt - 4 * half, hi = n - kb0 - 32 * kt - 4 * half;
 #pragma unroll
-                for (int r = 0; r < 16; ++r)
-                    if (8 * (r >> 2) + (r & 3) >= lim) s[kt][r] = -INFINITY;
+                for (int r = 0; r < 16; ++r) {
+                    const int row = 8 * (r >> 2) + (r & 3);
+                    if (row < lo || row >= hi) s[kt][r] = -INFINITY;
+                }
             }
         }
 
