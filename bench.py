@@ -281,6 +281,13 @@ def main():
     ap.add_argument("--op", choices=("forward", "backward", "split", "fp8"), default="forward")
     ap.add_argument("--splits", type=int, default=0, help="key ranges for --op split (0: suggested)")
     ap.add_argument("--seq-len", type=int, default=0, help="override the workload's N (0: keep it)")
+    ap.add_argument("--graph", action="store_true",
+                    help="time the K steps as one replay of a HIP graph holding them instead of "
+                         "back-to-back launches (both figures are then reported)")
+    ap.add_argument("--min-warmup-ms", type=float, default=200.0,
+                    help="after the W warm-up steps, keep warming up until this much time has "
+                         "passed: the chip's power controller takes about 10-15 ms of sustained "
+                         "load to settle its clock")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="also run a plain 512 MiB device copy (for HBM counter calibration)")
     args = ap.parse_args()
@@ -317,7 +324,7 @@ def main():
     stream = torch.cuda.current_stream(dev)
 
     def step():
-        fa.forward_into(qd, kd, vd, o, lse, w.scale, stream=stream)
+        fa.forward_into(qd, kd, vd, o, lse, w.scale, stream=None)
 
     fp8 = args.op == "fp8"
     if fp8:
@@ -328,7 +335,7 @@ def main():
         q, k, v = (torch.from_numpy(inputs.dequantize(c, s_)) for c, s_ in zip((q8, k8, v8), descale))
 
         def step():  # noqa: F811
-            fa.forward_fp8_into(q8d, k8d, v8d, descale, o, lse, w.scale, stream=stream)
+            fa.forward_fp8_into(q8d, k8d, v8d, descale, o, lse, w.scale, stream=None)
 
     if backward:
         do = inputs.make_grad(w)
@@ -338,7 +345,7 @@ def main():
         dws = torch.empty(qd.shape[:3], dtype=torch.float32, device=dev)
 
         def step():  # noqa: F811
-            fa.backward_into(qd, kd, vd, o, dod, lse, dq, dk, dv, dws, w.scale, stream=stream)
+            fa.backward_into(qd, kd, vd, o, dod, lse, dq, dk, dv, dws, w.scale, stream=None)
 
     split = args.op == "split"
     unsplit_ms = None
@@ -363,7 +370,7 @@ def main():
         unsplit_ms = time_it(step, args.steps)
 
         def step():  # noqa: F811
-            fa.forward_split_into(qd, kd, vd, o, lse, ws, splits, w.scale, stream=stream)
+            fa.forward_split_into(qd, kd, vd, o, lse, ws, splits, w.scale, stream=None)
 
     if args.calibrate_copy:
         src = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
@@ -372,17 +379,61 @@ def main():
             dst.copy_(src)
         torch.cuda.synchronize()
 
+    # Warm-up: W steps, then more until min-warmup-ms have passed, so that
+    # the timed steps run at the clock the power limit settles at (the first
+    # ~10 ms of sustained load run at a transient clock, up to 15 % slower).
+    warm_start = time.perf_counter()
+    warm_steps = 0
     for _ in range(args.warmup):
         step()
+        warm_steps += 1
     torch.cuda.synchronize()
-    start = torch.cuda.Event(enable_timing=True)
-    end = torch.cuda.Event(enable_timing=True)
-    start.record(stream)
-    for _ in range(args.steps):
-        step()
-    end.record(stream)
-    torch.cuda.synchronize()
-    ms = start.elapsed_time(end) / max(args.steps, 1)
+    while (time.perf_counter() - warm_start) * 1e3 < args.min_warmup_ms:
+        for _ in range(max(args.steps, 1)):
+            step()
+            warm_steps += 1
+        torch.cuda.synchronize()
+    warm_ms = (time.perf_counter() - warm_start) * 1e3
+
+    def timed(run):
+        start = torch.cuda.Event(enable_timing=True)
+        end = torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        start.record(stream)
+        run()
+        end.record(stream)
+        torch.cuda.synchronize()
+        return start.elapsed_time(end) / max(args.steps, 1)
+
+    def eager():
+        for _ in range(args.steps):
+            step()
+
+    # With --graph the K steps are captured once into a HIP graph (the
+    # library allocates nothing and records no memset), replayed once
+    # untimed, then timed as one replay, with no host work between the
+    # launches; the same K steps launched back to back are timed right after.
+    graph = None
+    if args.graph:
+        try:
+            graph = torch.cuda.CUDAGraph()
+            cap = torch.cuda.Stream(dev)
+            cap.wait_stream(stream)
+            with torch.cuda.graph(graph, stream=cap):
+                eager()
+            stream.wait_stream(cap)
+            graph.replay()
+            torch.cuda.synchronize()
+        except RuntimeError as exc:   # capture unavailable: time the launches themselves
+            print(f"graph capture failed ({exc}); timing back-to-back launches", file=sys.stderr)
+            graph = None
+            torch.cuda.synchronize()
+    if graph is not None:
+        ms = timed(graph.replay)
+        eager_ms = timed(eager)
+    else:
+        ms = timed(eager)
+        eager_ms = ms
 
     # Per-launch spread, after and outside the timed region: each launch
     # bracketed by its own pair of events on the launch stream.
@@ -437,6 +488,11 @@ def main():
         "config": {"workload": f"{w.name}: B={w.B} H={w.H} N={w.N} d={w.d} {w.dtype}, non-causal, "
                                f"scale=1/sqrt({w.d})" + (f", {kv_heads} K/V heads" if kv_heads != w.H else ""),
                    "B": w.B, "H": w.H, "N": w.N, "d": w.d, "causal": False, "kv_heads": kv_heads},
+        "timing": ("one replay of a HIP graph holding the K steps" if graph is not None
+                   else "K steps launched back to back"),
+        "eager_ms_per_step": round(eager_ms, 5),
+        "warmup_run": {"steps": warm_steps, "ms": round(warm_ms, 1),
+                       "note": "W steps, then more until --min-warmup-ms had passed"},
         "pct_of_mfma_peak": round(100 * tflops / peak, 2),
         "roofline": roof,
         "launch_ms": ({"median": round(per_ms[len(per_ms) // 2], 5), "min": round(per_ms[0], 5),
