@@ -375,8 +375,16 @@ flash_fwd_16(const T* __restrict__ Q, const T* __restrict__ K, const T* __restri
     if constexpr (KS == 1) {
         sweep3();
     } else {
-        if (kgrp == 0) sweep(Int<0>{});
-        else sweep(Int<1>{});
+        // Group 1's waves run at raised issue priority: with equal priority
+        // the older waves of group 0 go first on every SIMD, group 1 falls
+        // behind within each step and group 0 waits for it at the barrier.
+        if (kgrp == 0) {
+            sweep(Int<0>{});
+        } else {
+            __builtin_amdgcn_s_setprio(1);
+            sweep(Int<1>{});
+            __builtin_amdgcn_s_setprio(0);
+        }
     }
 
     if constexpr (KS > 1) {
