@@ -186,16 +186,22 @@ flash_bwd_dq(const T* __restrict__ Q, const T* __restrict__ K, const T* __restri
     // row-wise: swz_k.
     const int lrow = lane / CPR;
     const int lch = lane % CPR;
+    // One DMA form for every key tile: per-lane offsets within the tile
+    // plus a wave-uniform tile offset.  The ragged last tile's window ends at
+    // the last key (its rows below the tile's first key are masked: they
+    // belong to the previous tile); a sequence shorter than one tile reads
+    // zeros past its end (the per-lane offset is bounds checked).
+    auto tile_base = [&](int j0) { return min(j0, max(n - BC, 0)); };
     auto issue_loads = [&](int j0, auto stage) {
         constexpr int st = decltype(stage)::value;
         char* kdst = (st ? ks1 : ks0) + wave * UPW * 1024;
         char* vdst = (st ? vs1 : vs0) + wave * UPW * 1024;
+        const int so = __builtin_amdgcn_readfirstlane(tile_base(j0) * ROWB);
 #pragma unroll
         for (int i = 0; i < UPW; ++i) {
             const int r = (wave * UPW + i) * RPU + lrow;
-            const int g = min(j0 + r, n - 1) * ROWB;   // ragged last tile: re-read the last row
-            dma16(krs, kdst + i * 1024, g + 16 * (lch ^ swz_rt<D>(r)), 0);
-            dma16(vrs, vdst + i * 1024, g + 16 * (lch ^ swz_k<D>(r)), 0);
+            dma16(krs, kdst + i * 1024, r * ROWB + 16 * (lch ^ swz_rt<D>(r)), so);
+            dma16(vrs, vdst + i * 1024, r * ROWB + 16 * (lch ^ swz_k<D>(r)), so);
         }
     };
 
@@ -259,11 +265,12 @@ flash_bwd_dq(const T* __restrict__ Q, const T* __restrict__ K, const T* __restri
             qring[i % (2 * RQ)] = read_tr<ROWB>(kb, 16 * pc, to, dt);
         };
         static_for<0, 2 * RQ>([&](auto i) { read2(i); });
-        // P^T = exp2(S^T c - LSE log2 e); dS^T = P^T (dP^T - D).  Keys past
-        // the end (clamped rows of a ragged last tile) get dS = 0, in a branch
-        // taken by that tile only: one limit per sub-tile against the
-        // registers' constant row offsets, and the empty volatile asm keeps the
-        // compiler from turning it into selects that every tile executes.
+        // P^T = exp2(S^T c - LSE log2 e); dS^T = P^T (dP^T - D).  Rows of a
+        // ragged last tile that hold no key of it (below its first key, or
+        // zeros past the end) get dS = 0, in a branch taken by that tile only:
+        // two limits per sub-tile against the registers' constant row offsets,
+        // and the empty volatile asm keeps the compiler from turning it into
+        // selects that every tile executes.
 #pragma unroll
         for (int kt = 0; kt < KT; ++kt)
 #pragma unroll
@@ -273,12 +280,15 @@ flash_bwd_dq(const T* __restrict__ Q, const T* __restrict__ K, const T* __restri
             }
         if (j0 + BC > n) {
             asm volatile("");
+            const int kb = tile_base(j0);
 #pragma unroll
             for (int kt = 0; kt < KT; ++kt) {
-                const int lim = n - j0 - 32 * kt - 4 * half;
+                const int lo = j0 - kb - 32 * kt - 4 * half, hi = n - kb - 32 * kt - 4 * half;
 #pragma unroll
-                for (int r = 0; r < 16; ++r)
-                    if (8 * (r >> 2) + (r & 3) >= lim) s[kt][r] = 0.f;
+                for (int r = 0; r < 16; ++r) {
+                    const int row = 8 * (r >> 2) + (r & 3);
+                    if (row < lo || row >= hi) s[kt][r] = 0.f;
+                }
             }
         }
         u32x4 bsv[PC];
@@ -407,12 +417,18 @@ flash_bwd_dkdv(const T* __restrict__ Q, const T* __restrict__ K, const T* __rest
     // Units: wave w moves units w and w + 4 of the Q and dO tiles (QUNITS <= 8
     // each); wave 0 also stores LSE and D, loaded into a register one tile
     // earlier by load_lv (lanes 0..31: LSE, lanes 32..63: D).
+    // First query row held by the LDS tile of the query tile at i0: i0 for
+    // a full tile; the ragged last tile's window ends at the last query (its
+    // rows below i0 are masked, they belong to the previous tile); a sequence
+    // shorter than one tile starts at 0 and reads zeros past its end (the
+    // per-lane offset is bounds checked).  So every Q/dO DMA has one form.
+    auto qtile_base = [&](int i0) { return min(i0, max(n - BQ, 0)); };
     auto load_lv = [&](int h, int i0) {
         float lv = 0.f;
         if (wave == 0) {
             int ln;   // opaque lane copy: the per-lane address is not kept (and spilled) across the loop
             asm volatile("v_mov_b32 %0, %1" : "=v"(ln) : "v"(lane));
-            const int64_t rowi = ((int64_t)b * nh + h) * n + min(i0 + (ln & (BQ - 1)), n - 1);
+            const int64_t rowi = ((int64_t)b * nh + h) * n + min(qtile_base(i0) + (ln & (BQ - 1)), n - 1);
             lv = (ln < BQ ? LSE : Dr)[rowi];
         }
         return lv;
@@ -435,14 +451,15 @@ flash_bwd_dkdv(const T* __restrict__ Q, const T* __restrict__ K, const T* __rest
             __builtin_amdgcn_make_buffer_rsrc((void*)(Q + qbase), (short)0, n * ROWB, 0x00020000);
         const __amdgpu_buffer_rsrc_t ors =
             __builtin_amdgcn_make_buffer_rsrc((void*)(dO + qbase), (short)0, n * ROWB, 0x00020000);
+        const int so = __builtin_amdgcn_readfirstlane(qtile_base(i0) * ROWB);
 #pragma unroll
         for (int k = 0; k < 2; ++k) {
             const int u = wave + NW * k;
             if (u < QUNITS) {
                 const int r = u * RPU + lr;
-                const int gofs = min(i0 + r, n - 1) * ROWB + 16 * (lc ^ swz_rt<D>(r));
-                dma16(qrs, qd + u * 1024, gofs, 0);
-                dma16(ors, od + u * 1024, gofs, 0);
+                const int gofs = r * ROWB + 16 * (lc ^ swz_rt<D>(r));
+                dma16(qrs, qd + u * 1024, gofs, so);
+                dma16(ors, od + u * 1024, gofs, so);
             }
         }
     };
@@ -531,13 +548,17 @@ flash_bwd_dkdv(const T* __restrict__ Q, const T* __restrict__ K, const T* __rest
         }
         if (i0 + BQ > n) {
             asm volatile("");
-            const int lim = n - i0 - 4 * half;
+            // only rows [lo, hi) of a ragged query tile hold its queries
+            const int qb = qtile_base(i0);
+            const int lo = i0 - qb - 4 * half, hi = n - qb - 4 * half;
 #pragma unroll
-            for (int r = 0; r < 16; ++r)
-                if (8 * (r >> 2) + (r & 3) >= lim) {
+            for (int r = 0; r < 16; ++r) {
+                const int row = 8 * (r >> 2) + (r & 3);
+                if (row < lo || row >= hi) {
                     p[r] = 0.f;
                     ds[r] = 0.f;
                 }
+            }
         }
         const u32x4 bp[2] = {M::pack(&p[0]), M::pack(&p[8])};
         const u32x4 bs[2] = {M::pack(&ds[0]), M::pack(&ds[8])};
@@ -704,12 +725,18 @@ flash_bwd_dkdv_pp(const T* __restrict__ Q, const T* __restrict__ K, const T* __r
     // (first: a store after the DMAs would wait for them), then the Q and dO
     // units gw and gw + 4 of the tile.  Per-lane offsets come from an opaque
     // copy of the lane index, so that they are not kept across the loop.
+    // First query row held by the LDS tile of the query tile at i0: i0 for
+    // a full tile; the ragged last tile's window ends at the last query (its
+    // rows below i0 are masked, they belong to the previous tile); a sequence
+    // shorter than one tile starts at 0 and reads zeros past its end (the
+    // per-lane offset is bounds checked).  So every Q/dO DMA has one form.
+    auto qtile_base = [&](int i0) { return min(i0, max(n - BQ, 0)); };
     auto load_lv = [&](int h, int i0) {
         float lv = 0.f;
         if (wave == 4) {
             int ln;
             asm volatile("v_mov_b32 %0, %1" : "=v"(ln) : "v"(lane));
-            const int64_t rowi = ((int64_t)b * nh + h) * n + min(i0 + (ln & (BQ - 1)), n - 1);
+            const int64_t rowi = ((int64_t)b * nh + h) * n + min(qtile_base(i0) + (ln & (BQ - 1)), n - 1);
             lv = (ln < BQ ? LSE : Dr)[rowi];
         }
         return lv;
@@ -724,13 +751,14 @@ flash_bwd_dkdv_pp(const T* __restrict__ Q, const T* __restrict__ K, const T* __r
             __builtin_amdgcn_make_buffer_rsrc((void*)(Q + qbase), (short)0, n * ROWB, 0x00020000);
         const __amdgpu_buffer_rsrc_t ors =
             __builtin_amdgcn_make_buffer_rsrc((void*)(dO + qbase), (short)0, n * ROWB, 0x00020000);
+        const int so = __builtin_amdgcn_readfirstlane(qtile_base(i0) * ROWB);
 #pragma unroll
         for (int k = 0; k < 2; ++k) {
             const int u = gw + 4 * k;
             const int r = u * RPU + lr;
-            const int gofs = min(i0 + r, n - 1) * ROWB + 16 * (lc ^ swz_rt<D>(r));
-            dma16(qrs, qs + st * QTILEB + u * 1024, gofs, 0);
-            dma16(ors, os + st * QTILEB + u * 1024, gofs, 0);
+            const int gofs = r * ROWB + 16 * (lc ^ swz_rt<D>(r));
+            dma16(qrs, qs + st * QTILEB + u * 1024, gofs, so);
+            dma16(ors, os + st * QTILEB + u * 1024, gofs, so);
         }
     };
 
@@ -815,13 +843,17 @@ flash_bwd_dkdv_pp(const T* __restrict__ Q, const T* __restrict__ K, const T* __r
         }
         if (i0 + BQ > n) {
             asm volatile("");
-            const int lim = n - i0 - 4 * half;
+            // only rows [lo, hi) of a ragged query tile hold its queries
+            const int qb = qtile_base(i0);
+            const int lo = i0 - qb - 4 * half, hi = n - qb - 4 * half;
 #pragma unroll
-            for (int r = 0; r < 16; ++r)
-                if (8 * (r >> 2) + (r & 3) >= lim) {
+            for (int r = 0; r < 16; ++r) {
+                const int row = 8 * (r >> 2) + (r & 3);
+                if (row < lo || row >= hi) {
                     p[r] = 0.f;
                     ds[r] = 0.f;
                 }
+            }
         }
         bp[0] = M::pack(&p[0]);
         bp[1] = M::pack(&p[8]);
