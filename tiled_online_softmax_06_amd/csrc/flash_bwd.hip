@@ -120,16 +120,20 @@ flash_bwd_dot(const T* __restrict__ O, const T* __restrict__ dO, float* __restri
 }
 
 // ---------------------------------------------------------------------------
-// dQ.  Workgroup: 4 waves x 32 query rows of one (b, h); K/V tiles of 64 keys.
+// dQ.  Workgroup: NW waves x 32 query rows of one (b, h); K/V tiles of 64
+// keys.  d = 128: 8 waves (one workgroup per CU), so that each K/V tile
+// brought into LDS serves 256 query rows, through a three-stage ring;
+// d = 64: 4 waves, three workgroups per CU, two stages.
 // ---------------------------------------------------------------------------
 template <typename T, int D>
-__global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2)))
+__global__ void __launch_bounds__(D == 128 ? 512 : 256) __attribute__((amdgpu_waves_per_eu(2)))
 flash_bwd_dq(const T* __restrict__ Q, const T* __restrict__ K, const T* __restrict__ V,
              const T* __restrict__ dO, const float* __restrict__ LSE, const float* __restrict__ Dr,
              T* __restrict__ dQ, int n, int qtiles, int total, float c, float scale, int nh, int grp)
 {
     using M = Mfma<T>;
-    constexpr int NW = 4;
+    constexpr int NW = D == 128 ? 8 : 4;
+    constexpr int NST = D == 128 ? 3 : 2;    // LDS stages of the K/V ring
     constexpr int BC = 64;
     constexpr int BR = 32 * NW;
     constexpr int ROWB = D * 2;
@@ -148,6 +152,16 @@ flash_bwd_dq(const T* __restrict__ Q, const T* __restrict__ K, const T* __restri
     __shared__ __attribute__((aligned(1024))) char vs0[TILEB];
     __shared__ __attribute__((aligned(1024))) char ks1[TILEB];
     __shared__ __attribute__((aligned(1024))) char vs1[TILEB];
+    __shared__ __attribute__((aligned(1024))) char ks2[NST > 2 ? TILEB : 16];
+    __shared__ __attribute__((aligned(1024))) char vs2[NST > 2 ? TILEB : 16];
+    auto kst = [&](auto stage) -> char* {
+        constexpr int st = decltype(stage)::value;
+        return st == 0 ? ks0 : st == 1 ? ks1 : ks2;
+    };
+    auto vst = [&](auto stage) -> char* {
+        constexpr int st = decltype(stage)::value;
+        return st == 0 ? vs0 : st == 1 ? vs1 : vs2;
+    };
 
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -193,9 +207,8 @@ flash_bwd_dq(const T* __restrict__ Q, const T* __restrict__ K, const T* __restri
     // zeros past its end (the per-lane offset is bounds checked).
     auto tile_base = [&](int j0) { return min(j0, max(n - BC, 0)); };
     auto issue_loads = [&](int j0, auto stage) {
-        constexpr int st = decltype(stage)::value;
-        char* kdst = (st ? ks1 : ks0) + wave * UPW * 1024;
-        char* vdst = (st ? vs1 : vs0) + wave * UPW * 1024;
+        char* kdst = kst(stage) + wave * UPW * 1024;
+        char* vdst = vst(stage) + wave * UPW * 1024;
         const int so = __builtin_amdgcn_readfirstlane(tile_base(j0) * ROWB);
 #pragma unroll
         for (int i = 0; i < UPW; ++i) {
@@ -226,9 +239,8 @@ flash_bwd_dq(const T* __restrict__ Q, const T* __restrict__ K, const T* __restri
     constexpr int RQ = 1;
     u32x4 qring[2 * RQ];
     auto compute = [&](auto stage, int j0) {
-        constexpr int st = decltype(stage)::value;
-        const char* kb = st ? ks1 : ks0;
-        const char* vb = st ? vs1 : vs0;
+        const char* kb = kst(stage);
+        const char* vb = vst(stage);
         int ko = koff, vo = voff, to = ktr;
         asm volatile("" : "+v"(ko), "+v"(vo), "+v"(to));
         constexpr int N1 = KT * KC;
@@ -313,18 +325,52 @@ flash_bwd_dq(const T* __restrict__ Q, const T* __restrict__ K, const T* __restri
     };
 
     const int ntiles = (n + BC - 1) / BC;
-    issue_loads(0, Int<0>{});
-    for (int t = 0;;) {
-        __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0): this wave's DMA landed
-        __syncthreads();                      // ... every wave's; stage 1 is free
-        if (t + 1 < ntiles) issue_loads((t + 1) * BC, Int<1>{});
-        compute(Int<0>{}, t * BC);
-        if (++t == ntiles) break;
-        __builtin_amdgcn_s_waitcnt(0x0F70);
-        __syncthreads();
-        if (t + 1 < ntiles) issue_loads((t + 1) * BC, Int<0>{});
-        compute(Int<1>{}, t * BC);
-        if (++t == ntiles) break;
+    if constexpr (NST == 2) {
+        issue_loads(0, Int<0>{});
+        for (int t = 0;;) {
+            __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0): this wave's DMA landed
+            __syncthreads();                      // ... every wave's; stage 1 is free
+            if (t + 1 < ntiles) issue_loads((t + 1) * BC, Int<1>{});
+            compute(Int<0>{}, t * BC);
+            if (++t == ntiles) break;
+            __builtin_amdgcn_s_waitcnt(0x0F70);
+            __syncthreads();
+            if (t + 1 < ntiles) issue_loads((t + 1) * BC, Int<0>{});
+            compute(Int<1>{}, t * BC);
+            if (++t == ntiles) break;
+        }
+    } else {
+        // Three stages: tile t in stage t mod 3; the DMA of tile t + 2 goes
+        // out at the top of step t into the stage of tile t - 1, which every
+        // wave finished reading in step t - 1.  Each wave waits only for tile
+        // t's DMA (tile t + 1's, 2 UPW instructions, may still be in flight)
+        // before a barrier without a fence (a fence waits for every load).
+        // Tiles past the end are loaded too (never read), and the loop has
+        // one exit, so the compiler's tracking of the loads stays exact.
+        issue_loads(0, Int<0>{});
+        issue_loads(BC, Int<1>{});
+        static_assert(2 * UPW <= 15, "wait count below");
+        auto stepk = [&](int t, auto stage) __attribute__((always_inline)) {
+            constexpr int S = decltype(stage)::value;
+            __builtin_amdgcn_s_waitcnt(0x0070 | (2 * UPW));   // vmcnt(2 UPW) lgkmcnt(0)
+            __builtin_amdgcn_sched_barrier(0);
+            asm volatile("" ::: "memory");
+            __builtin_amdgcn_s_barrier();
+            asm volatile("" ::: "memory");
+            __builtin_amdgcn_sched_barrier(0);
+            issue_loads((t + 2) * BC, Int<(S + 2) % 3>{});
+            compute(stage, t * BC);
+        };
+        stepk(0, Int<0>{});
+        int t = 1;
+        for (; t + 3 <= ntiles; t += 3) {
+            stepk(t, Int<1>{});
+            stepk(t + 1, Int<2>{});
+            stepk(t + 2, Int<0>{});
+        }
+        if (t < ntiles) stepk(t++, Int<1>{});
+        if (t < ntiles) stepk(t++, Int<2>{});
+        __builtin_amdgcn_s_waitcnt(0x0070);       // no DMA into LDS left in flight
     }
 
     if (qrow < n) {
@@ -1000,11 +1046,13 @@ hipError_t launch_bwd_t(const BwdArgs& a, hipStream_t stream) {
     }
     // 2. dQ
     {
-        const int qtiles = (int)((a.n + 127) / 128);
+        constexpr int nwq = D == 128 ? 8 : 4;   // waves (32 query rows each) per workgroup
+        const int qtiles = (int)((a.n + 32 * nwq - 1) / (32 * nwq));
         const int total = (int)(a.bh * qtiles);
         void* args[] = {&q, &k, &v, &dout, &lse, &dr, &dq, (void*)&n, (void*)&qtiles, (void*)&total,
                         (void*)&c, (void*)&scale, (void*)&nh, (void*)&grp};
-        hipError_t e = hipLaunchKernel((const void*)&flash_bwd_dq<T, D>, dim3(total), dim3(256), args, 0, stream);
+        hipError_t e = hipLaunchKernel((const void*)&flash_bwd_dq<T, D>, dim3(total), dim3(64 * nwq), args, 0,
+                                       stream);
         if (e != hipSuccess) return e;
     }
     // 3. dK, dV: at d = 128 the two-group kernel (256 keys per workgroup),
