@@ -74,11 +74,14 @@ def full_case(B, H, Hkv, N, d, dtype, seed, scale=None):
 
 @pytest.mark.parametrize("dtype", ["fp16", "bf16"])
 @pytest.mark.parametrize("d", [64, 128])
-@pytest.mark.parametrize("N", [1, 65, 77, 256, 300])
+@pytest.mark.parametrize("N", [1, 65, 77, 129, 192, 256, 300, 384])
 def test_backward_ragged_lengths(dtype, d, N):
     """Lengths below one tile, a last key tile and a last 32-row query block
     holding a single valid row (N = 65), a ragged block, exact tiles and a
-    ragged tail over several tiles."""
+    ragged tail over several tiles.  The dQ kernel at d = 128 streams its
+    64-key tiles through three LDS stages: 1, 2, 3, 4, 5 and 6 key tiles
+    (N = 1, 65, 129 and 192, 256, 300, 384) end its loop on every stage and
+    every remainder of the tile count modulo 3."""
     full_case(1, 2, 2, N, d, dtype, seed=50 + N + d)
 
 

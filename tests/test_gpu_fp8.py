@@ -62,10 +62,14 @@ def fp8_case(B, H, Hkv, N, d, seed, out="bf16", scale=None, sigma=1.0):
 
 
 @pytest.mark.parametrize("d", [64, 128])
-@pytest.mark.parametrize("N", [1, 65, 77, 256, 1000])
+@pytest.mark.parametrize("N", [1, 64, 65, 77, 127, 256, 1000])
 def test_fp8_matches_oracle(d, N):
     """N = 65: the last 64-key tile holds a single valid key (the masking
-    branch with every other key of both 32-key sub-tiles past the end)."""
+    branch with every other key of both 32-key sub-tiles past the end).
+    The ragged last tile is loaded as the window of the last 64 keys, its
+    rows below the tile's first key masked: N = 65 and 127 mask 63 and 1 of
+    them, N = 64 and 256 end on a whole tile, N = 1 and 77 are shorter than
+    or just past one tile."""
     fp8_case(1, 2, 2, N, d, seed=500 + N + d)
 
 

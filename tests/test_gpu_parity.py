@@ -130,6 +130,24 @@ def test_ragged_lengths(dtype, d):
         check(o, lse, ref_o, ref_lse, dtype, f"{dtype} d={d} N={n}")
 
 
+@pytest.mark.parametrize("N", [100, 128, 129, 192, 250, 320, 383])
+def test_d64_three_stage_ring_tile_counts(N):
+    """d = 64 with more than 256 workgroups of 128 query rows (270 heads):
+    the kernel that streams K/V tiles through three LDS stages, two tiles
+    ahead, and runs the last one or two steps after its loop.  The key-tile
+    counts 2, 2, 3, 3, 4, 5, 6 cover every remainder modulo 3, with whole
+    (128, 192, 320) and ragged (100, 129, 250, 383) last tiles."""
+    dtype = "bf16" if N % 2 else "fp16"
+    B, H, d = 3, 90, 64
+    assert B * H * ((N + 127) // 128) > 256
+    q, k, v = inputs.random_qkv((B, H, N, d), dtype, seed=900 + N)
+    scale = 1.0 / math.sqrt(d)
+    print(f"case B={B} H={H} N={N} d={d} {dtype}", flush=True)
+    o, lse = run(q, k, v, scale)
+    ref_o, ref_lse = oracle_threads(q, k, v, scale)
+    check(o, lse, ref_o, ref_lse, dtype, f"{dtype} d=64 N={N} (270 heads)")
+
+
 @pytest.mark.parametrize("dtype", ["fp32", "bf16"])
 def test_single_key_gives_v(dtype):
     """N = 1: the only weight is 1, so O = V and LSE = scale * q.k.  bf16
