@@ -21,12 +21,14 @@
 //
 // Kernels:
 //   flash_bwd_dot   D_i = <dO_i, O_i> in fp32 (one row per 16 lanes).
-//   flash_bwd_dq    4 waves x 32 query rows; K/V tiles of 64 keys streamed
-//                   through LDS (the forward kernel's structure):
+//   flash_bwd_dq    8 waves (d = 128) or 4 (d = 64) x 32 query rows; K/V
+//                   tiles of 64 keys streamed through a three-stage (d = 128)
+//                   or two-stage LDS ring:
 //                   S^T = K Q^T, P^T, dP^T = V dO^T, dS^T, dQ^T += K^T dS^T.
-//   flash_bwd_dkdv  4 waves x 32 keys; Q/dO tiles of 32 queries streamed
-//                   through LDS: S = Q K^T, P, dP = dO V^T, dS,
-//                   dV^T += dO^T P, dK^T += Q^T dS.
+//   flash_bwd_dkdv_pp (d = 128) 8 waves x 32 keys in two groups one phase
+//                   apart; flash_bwd_dkdv (d = 64) 4 waves x 32 keys; Q/dO
+//                   tiles of 32 queries streamed through LDS: S = Q K^T, P,
+//                   dP = dO V^T, dS, dV^T += dO^T P, dK^T += Q^T dS.
 // Every product runs on v_mfma_f32_32x32x16_{bf16,f16} with fp32
 // accumulation; weights P and dS are rounded to the input type for the
 // second products.  An accumulator (lane = column, registers = rows) feeds
