@@ -248,6 +248,46 @@ def test_deterministic():
     assert torch.equal(o1, o2) and torch.equal(l1, l2)
 
 
+def test_concurrent_streams_match_serial():
+    """A forward and a backward call in flight at once on two streams (both
+    at the default priority), three rounds without synchronising in
+    between, give the same bits as the same calls run one after another:
+    the entry points used keep no state between calls."""
+    q1, k1, v1 = (t.to(DEV) for t in inputs.random_qkv((2, 8, 2048, 128), "bf16", seed=61))
+    q2, k2, v2 = (t.to(DEV) for t in inputs.random_qkv((2, 6, 1000, 64), "fp16", seed=62, kv_heads=3))
+    do2 = inputs.random_grad((2, 6, 1000, 64), "fp16", 63).to(DEV)
+    s1, s2 = 1 / math.sqrt(128), 1 / math.sqrt(64)
+    o2, l2 = fa.forward(q2, k2, v2, s2)
+
+    def outputs():
+        o1 = torch.empty_like(q1)
+        lse1 = torch.empty(q1.shape[:3], dtype=torch.float32, device=DEV)
+        g = [torch.empty_like(q2), torch.empty_like(k2), torch.empty_like(v2),
+             torch.empty(q2.shape[:3], dtype=torch.float32, device=DEV)]
+        return (o1, lse1), g
+
+    # serial reference on the current stream
+    (ro1, rl1), rg = outputs()
+    fa.forward_into(q1, k1, v1, ro1, rl1, s1)
+    fa.backward_into(q2, k2, v2, o2, do2, l2, *rg, s2)
+    torch.cuda.synchronize()
+
+    a, b = torch.cuda.Stream(), torch.cuda.Stream()
+    torch.cuda.current_stream().synchronize()
+    results = []
+    for _ in range(3):
+        (o1, lse1), g = outputs()
+        torch.cuda.synchronize()            # outputs allocated before either stream runs
+        fa.forward_into(q1, k1, v1, o1, lse1, s1, stream=a)
+        fa.backward_into(q2, k2, v2, o2, do2, l2, *g, s2, stream=b)
+        results.append(((o1, lse1), g))
+    torch.cuda.synchronize()
+    for i, ((o1, lse1), g) in enumerate(results):
+        assert torch.equal(o1, ro1) and torch.equal(lse1, rl1), f"forward, round {i}"
+        for name, x, y in zip(("dQ", "dK", "dV", "D"), g, rg):
+            assert torch.equal(x, y), f"backward {name}, round {i}"
+
+
 def test_side_stream():
     """Launch on a non-default stream; results equal the default-stream run."""
     q, k, v = inputs.random_qkv((2, 4, 640, 64), "fp16", seed=12)
